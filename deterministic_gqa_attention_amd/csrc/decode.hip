@@ -1,0 +1,218 @@
+// Paged-KV decode, pass 1 (gfx950): one workgroup per (sequence, kv head,
+// KV block) computes the block's partial state for the q heads of the group
+// and writes it to the caller's workspace; pass 2 (fold.hip) folds the items
+// of each row in ascending block index.
+//
+// Keys are gathered through the page table: key j of sequence s is slot j % P
+// of page page_table[s][j / P] in a pool laid out [page][kv head][slot][dim].
+// The per-(row, block) arithmetic is the same as in the prefill kernel (same
+// MFMA shape and operand order, same softmax tree, same PV chain), only split
+// over the four waves: wave w computes score sub-tile w and output dim tile w,
+// and the block max, sub-tile sums and bf16 P go through LDS.  Rows are the
+// group's q heads for the one query token (columns >= G are zero padding).
+#include "kernels.hpp"
+#include "tile.hpp"
+
+namespace rla {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+template <int BK, bool F32>
+struct DecodeLds {
+  static constexpr int NKT = BK / 32;
+  static constexpr int kV = TileLayout<BK>::kVBytes;
+  static constexpr int kPBytesPerTile = 64 * 32 * (F32 ? 2 : 1);  // 64 lanes x 16 bf16 (x2 hi/lo)
+  static constexpr int kPOff = kV;
+  static constexpr int kMaxOff = kPOff + NKT * kPBytesPerTile;
+  static constexpr int kSumOff = kMaxOff + NKT * 32 * 4;
+  static constexpr int kBytes = kSumOff + NKT * 32 * 4;
+};
+
+// Element offset of key `key` of sequence `seq`, kv head hk, in the pool.
+// key < len <= len_cap <= max_pages * P keeps the table read in its row; a
+// page id outside [0, num_pages) is never dereferenced (ok = false).
+__device__ __forceinline__ int64_t page_row_off(const DecodeArgs& a, int seq, int hk, int64_t key, bool& ok) {
+  const int32_t page = a.page_table[static_cast<int64_t>(seq) * a.max_pages + key / a.P];
+  ok = page >= 0 && page < a.num_pages;
+  return ((static_cast<int64_t>(ok ? page : 0) * a.Hkv + hk) * a.P + key % a.P) * kHeadDim;
+}
+
+template <int BK, bool F32>
+__global__ __launch_bounds__(kThreads) void decode_items_kernel(const DecodeArgs a) {
+  using Lay = DecodeLds<BK, F32>;
+  constexpr int NKT = Lay::NKT;
+  __shared__ __attribute__((aligned(16))) char lds[Lay::kBytes];
+  char* lv = lds;
+  char* lp = lds + Lay::kPOff;
+  float* red_max = reinterpret_cast<float*>(lds + Lay::kMaxOff);
+  float* red_sum = reinterpret_cast<float*>(lds + Lay::kSumOff);
+
+  const int64_t x = blockIdx.x;
+  const int hk = static_cast<int>(x % a.Hkv);
+  const int seq = static_cast<int>((x / a.Hkv) % a.Bd);
+  const int64_t blk = x / (static_cast<int64_t>(a.Hkv) * a.Bd);
+  int64_t len = a.ctx_lens[seq];
+  len = len < 0 ? 0 : (len > a.len_cap ? a.len_cap : len);
+  const int64_t nb = (len + BK - 1) / BK;
+  if (blk >= nb) return;  // uniform across the workgroup
+  const int64_t key0 = blk * BK;
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int col = lane & 31;
+  const int half = lane >> 5;
+
+  // ---- stage V^T for the block (all threads), gathered through the page table
+  {
+    constexpr int VIT = BK / 64;
+    const int dc = tid & 15;
+    const int kg0 = tid >> 4;
+    u32x4 vx[VIT][4];
+#pragma unroll
+    for (int i = 0; i < VIT; ++i) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t key = key0 + 4 * (kg0 + 16 * i) + j;
+        vx[i][j] = u32x4{0, 0, 0, 0};
+        if (key < len) {
+          bool ok;
+          const int64_t off = page_row_off(a, seq, hk, key, ok);
+          if (ok) vx[i][j] = gload16(a.v_pool + off + dc * 8);
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < VIT; ++i) {
+      u32x2 tt[8];
+      transpose4x8(vx[i], tt);
+      const int kg = kg0 + 16 * i;
+#pragma unroll
+      for (int ii = 0; ii < 8; ++ii) lds_store8(lv, TileLayout<BK>::v_off(8 * dc + ii, kg), tt[ii]);
+    }
+  }
+
+  // ---- scores of sub-tile kt = wave (waves < NKT)
+  f32x16 s = f32x16{};
+  float m_lane = kNegInf;
+  if (wave < NKT) {
+    bf16x8 kf[kDSteps];
+    bf16x8 qf[kDSteps];
+    const int64_t key = key0 + wave * 32 + col;
+    bool kok = false;
+    int64_t koff = 0;
+    if (key < len) {
+      koff = page_row_off(a, seq, hk, key, kok);
+    }
+    const bool qok = col < a.G;
+    const uint16_t* qrow = a.q + (static_cast<int64_t>(seq) * a.Hq + hk * a.G + col) * kHeadDim + 8 * half;
+#pragma unroll
+    for (int ds = 0; ds < kDSteps; ++ds) {
+      kf[ds] = as_bf16x8(kok ? gload16(a.k_pool + koff + 16 * ds + 8 * half) : u32x4{0, 0, 0, 0});
+      qf[ds] = as_bf16x8(qok ? gload16(qrow + 16 * ds) : u32x4{0, 0, 0, 0});
+    }
+#pragma unroll
+    for (int ds = 0; ds < kDSteps; ++ds) s = mfma(kf[ds], qf[ds], s);
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int64_t kk = key0 + wave * 32 + acc_row(v, half);
+      float t = s[v] * a.c;
+      t = kk < len ? t : kNegInf;
+      s[v] = t;
+      m_lane = fmaxf(m_lane, t);
+    }
+    m_lane = fmaxf(m_lane, partner(m_lane));
+    if (half == 0) red_max[wave * 32 + col] = m_lane;
+  }
+  __syncthreads();
+
+  float m_t = red_max[col];
+#pragma unroll
+  for (int kt = 1; kt < NKT; ++kt) m_t = fmaxf(m_t, red_max[kt * 32 + col]);
+  const float m_use = (m_t == kNegInf) ? 0.0f : m_t;
+
+  if (wave < NKT) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) s[v] = hw_exp2(s[v] - m_use);
+    const float aa = tree16(s);
+    const float sum = aa + partner(aa);
+    if (half == 0) red_sum[wave * 32 + col] = sum;
+    u32x4 ph[2], pl[2];
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float p0 = s[8 * st + 2 * w];
+        const float p1 = s[8 * st + 2 * w + 1];
+        const uint32_t h = pack_bf16(p0, p1);
+        ph[st][w] = h;
+        if constexpr (F32) {
+          const float r0 = p0 - bf16_lo_to_f32(h);
+          const float r1 = p1 - bf16_hi_to_f32(h);
+          pl[st][w] = pack_bf16(r0, r1);
+        }
+      }
+    }
+    char* my = lp + wave * Lay::kPBytesPerTile + lane * (F32 ? 64 : 32);
+    lds_store16(my, 0, ph[0]);
+    lds_store16(my, 16, ph[1]);
+    if constexpr (F32) {
+      lds_store16(my, 32, pl[0]);
+      lds_store16(my, 48, pl[1]);
+    }
+  }
+  __syncthreads();
+
+  float sub[NKT];
+#pragma unroll
+  for (int kt = 0; kt < NKT; ++kt) sub[kt] = red_sum[kt * 32 + col];
+  const float l_b = combine_subtiles<NKT>(sub);
+
+  // ---- PV for output dim tile dt = wave
+  const int dt = wave;
+  f32x16 acc = f32x16{};
+#pragma unroll
+  for (int kt = 0; kt < NKT; ++kt) {
+    const char* pp = lp + kt * Lay::kPBytesPerTile + lane * (F32 ? 64 : 32);
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      const bf16x8 vf = v_frag<BK>(lv, dt, kt, st, col, half);
+      acc = mfma(vf, as_bf16x8(lds_load16(pp, 16 * st)), acc);
+      if constexpr (F32) acc = mfma(vf, as_bf16x8(lds_load16(pp, 32 + 16 * st)), acc);
+    }
+  }
+  const ItemScalars sc = item_scalars(m_t, l_b);
+  if (col < a.G) {
+    const int head = hk * a.G + col;
+    const int64_t item = (static_cast<int64_t>(seq) * a.max_blocks + blk) * a.Hq + head;
+    float* po = a.items_out + item * kHeadDim;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int d = dt * 32 + 8 * g + 4 * half;
+      *reinterpret_cast<f32x4*>(po + d) = f32x4{item_out(acc[4 * g], sc), item_out(acc[4 * g + 1], sc),
+                                                item_out(acc[4 * g + 2], sc), item_out(acc[4 * g + 3], sc)};
+    }
+    if (wave == 0 && half == 0) a.items_lse[item] = sc.L;
+  }
+}
+
+template <int BK, bool F32>
+hipError_t launch_t(const DecodeArgs& a, hipStream_t s) {
+  const int64_t grid = static_cast<int64_t>(a.max_blocks) * a.Bd * a.Hkv;
+  if (grid <= 0) return hipSuccess;
+  if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((decode_items_kernel<BK, F32>), dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode_items(const DecodeArgs& a, int block, bool out_f32, hipStream_t s) {
+  if (block == 128) return out_f32 ? launch_t<128, true>(a, s) : launch_t<128, false>(a, s);
+  if (block == 64) return out_f32 ? launch_t<64, true>(a, s) : launch_t<64, false>(a, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace rla

@@ -1,0 +1,76 @@
+// Internal launch interface between the C ABI (api.cpp) and the kernels.
+// Plain structs passed by value as kernel arguments; all pointers are device
+// pointers.  Tensors are bf16 bit patterns (uint16_t) unless noted.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rla {
+
+constexpr int kHeadDimPublic = 128;  // the only head dimension the kernels implement
+constexpr int kMaxParts = 512;  // partial states per merge / owned blocks per emit launch
+
+// Prefill and chunked prefill.  Query row t of batch b sits at absolute
+// position pos0 + t; it attends keys [0, kv_len) (and key <= position when
+// causal).  Layouts: q rows at q + b*q_bstride + (t*Hq + h)*D; keys at
+// k + b*kv_bstride + (key*Hkv + hk)*D; outputs out/lse as [B][Sq][Hq](D).
+struct PrefillArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  void* out;                 // bf16 or fp32 [B][Sq][Hq][D] (fused mode)
+  float* lse;                // [B][Sq][Hq] (fused mode)
+  float* part_out;           // emit mode: [n_emit][B*Sq][Hq][D]
+  float* part_lse;           // emit mode: [n_emit][B*Sq][Hq]
+  int64_t q_bstride;         // elements between batches of q
+  int64_t kv_bstride;        // elements between batches of k / v
+  int64_t pos0;
+  int64_t kv_len;
+  int32_t B, Sq, Hq, Hkv, G;
+  int32_t heads_per_wg;      // q heads of one group handled by one workgroup
+  int32_t pos_groups;        // 32-row position groups per workgroup
+  int32_t hsubs;             // workgroups needed to cover one group's heads
+  int32_t n_ptiles;          // position tiles of 32*pos_groups rows
+  int32_t causal;
+  float c;                   // softmax_scale * log2(e), rounded to fp32
+  int32_t n_emit;            // emit mode: number of owned blocks
+  uint16_t emit_blocks[kMaxParts];
+};
+
+// Paged decode, pass 1: one workgroup per (sequence, kv head, 128- or 64-key
+// block) writes the block's partial state for the group's q heads.
+struct DecodeArgs {
+  const uint16_t* q;          // [Bd][Hq][D]
+  const uint16_t* k_pool;     // [num_pages][Hkv][P][D]
+  const uint16_t* v_pool;
+  const int32_t* page_table;  // [Bd][max_pages]
+  const int32_t* ctx_lens;    // [Bd]
+  float* items_out;           // [Bd][max_blocks][Hq][D]
+  float* items_lse;           // [Bd][max_blocks][Hq]
+  int64_t num_pages;
+  int32_t P, max_pages, Bd, Hq, Hkv, G, max_blocks, len_cap;
+  float c;
+};
+
+// Fold of per-block partial states in ascending block order (decode pass 2)
+// or in a given order over an explicit list of parts (merge).
+struct FoldArgs {
+  const float* part_out;      // merge: [n_parts][rows][Hq][D]; decode: items
+  const float* part_lse;
+  const int32_t* ctx_lens;    // decode: [Bd] (block count per row); merge: null
+  void* out;                  // [rows][Hq][D] bf16 or fp32
+  float* lse;                 // [rows][Hq]
+  int64_t rows;
+  int32_t Hq;
+  int32_t n_parts;            // merge: parts to fold; decode: max_blocks
+  int32_t block;              // decode: keys per block; merge: unused
+  int32_t len_cap;            // decode: clamp on context lengths
+  uint16_t order[kMaxParts];  // merge: part indices in fold order
+};
+
+hipError_t launch_prefill(const PrefillArgs& a, int block, bool out_f32, bool emit, hipStream_t s);
+hipError_t launch_decode_items(const DecodeArgs& a, int block, bool out_f32, hipStream_t s);
+hipError_t launch_fold(const FoldArgs& a, bool decode, bool out_f32, hipStream_t s);
+
+}  // namespace rla

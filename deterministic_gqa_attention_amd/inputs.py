@@ -33,12 +33,26 @@ TID_Q, TID_K, TID_V, TID_LENS, TID_PAGES, TID_RELOC, TID_ARRIVAL = 1, 2, 3, 4, 5
 
 
 def f64_to_bf16_bits(x: np.ndarray) -> np.ndarray:
-    """FP64 -> FP32 (RNE) -> bf16 (RNE) bit patterns as uint16.  NaN stays NaN."""
+    """FP64 -> FP32 (RNE) -> bf16 (RNE) bit patterns as uint16.  NaN stays NaN.
+
+    Both roundings are done by torch's CPU conversions (IEEE round-to-nearest-
+    even, vectorised and multithreaded); ``f64_to_bf16_bits_reference`` is the
+    same rounding written out in numpy, and the tests check the two agree."""
+    import torch
+
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float64))
+    return t.to(torch.float32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def f64_to_bf16_bits_reference(x: np.ndarray) -> np.ndarray:
+    """Numpy statement of the same rounding: FP64 -> FP32 by the hardware cast,
+    then add 0x7FFF plus the lowest kept bit and truncate (uint32 cannot wrap
+    for a non-NaN input); NaN -> 0x7FC0."""
     f = np.ascontiguousarray(x, dtype=np.float64).astype(np.float32)
-    u = f.view(np.uint32).astype(np.uint64)
-    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    u = f.view(np.uint32)
+    lsb = (u >> np.uint32(16)) & np.uint32(1)
+    out = ((u + np.uint32(0x7FFF) + lsb) >> np.uint32(16)).astype(np.uint16)
     nan = np.isnan(f)
-    out = rounded.astype(np.uint16)
     if nan.any():
         out[nan] = 0x7FC0
     return out
@@ -223,6 +237,8 @@ def decode_inputs(cfg: DecodeConfig, *, lengths=None, num_pages=None):
     table = np.full((Bd, max_pages), -1, np.int32)
     k_pool = np.zeros((num_pages, Hkv, P, D), np.uint16)
     v_pool = np.zeros((num_pages, Hkv, P, D), np.uint16)
+    # one reusable FP64 buffer (fresh per-sequence allocations dominate the cost otherwise)
+    buf = np.empty((int(need.max(initial=0)) * P, Hkv, D), np.float64)
     cursor = 0
     for s in range(Bd):
         n = int(need[s])
@@ -230,15 +246,12 @@ def decode_inputs(cfg: DecodeConfig, *, lengths=None, num_pages=None):
         cursor += n
         table[s, :n] = pages
         L = int(lens[s])
-        ks = draw_bf16([1000 * cfg.cfg_id + TID_K, s], (L, Hkv, D))
-        vs = draw_bf16([1000 * cfg.cfg_id + TID_V, s], (L, Hkv, D))
-        pad = n * P - L
-        if pad:
-            ks = np.concatenate([ks, np.zeros((pad, Hkv, D), np.uint16)])
-            vs = np.concatenate([vs, np.zeros((pad, Hkv, D), np.uint16)])
-        # [n*P, Hkv, D] -> [n, P, Hkv, D] -> [n, Hkv, P, D]
-        k_pool[pages] = ks.reshape(n, P, Hkv, D).transpose(0, 2, 1, 3)
-        v_pool[pages] = vs.reshape(n, P, Hkv, D).transpose(0, 2, 1, 3)
+        for seed_tid, pool in ((TID_K, k_pool), (TID_V, v_pool)):
+            x = buf[: n * P]
+            np.random.Generator(np.random.PCG64([1000 * cfg.cfg_id + seed_tid, s])).standard_normal(out=x[:L])
+            x[L:] = 0.0
+            # [n*P, Hkv, D] -> [n, P, Hkv, D] -> [n, Hkv, P, D]
+            pool[pages] = f64_to_bf16_bits(x).reshape(n, P, Hkv, D).transpose(0, 2, 1, 3)
     q = draw_bf16(1000 * cfg.cfg_id + TID_Q, (Bd, cfg.Hq, D))
     return {"q": q, "k_pool": k_pool, "v_pool": v_pool, "page_table": table, "ctx_lens": lens}
 

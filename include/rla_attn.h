@@ -1,0 +1,182 @@
+/*
+ * rla_attn.h — C ABI of the deterministic grouped-query attention library for
+ * AMD MI355X (gfx950), librla_attn.so.
+ *
+ * What it computes.  Forward attention for grouped-query heads (q head h reads
+ * kv head h / (Hq / Hkv)) on post-RoPE bf16 inputs, with FP32 accumulation,
+ * per-KV-block partial states (out_i, lse_i) that are combined in ascending
+ * global block index, and a downcast to bf16 only at the final write.  The
+ * pages that specify it: "WS2 Attention PR5 Drift Benchmark" (sections
+ * "Scope": Qwen3-8B target Hq=32, Hkv=8, D=128, TP head shards, CP=1/2, full
+ * and chunked prefill, BF16 path vs FP32 reference; "Transformer Engine
+ * Reuse": partial state = (out_i, lse_i, global_block_index_i), sorted by
+ * global_block_index before the online-softmax correction; "Report Contract":
+ * merge order always global_block_index, downcast at the final write) and
+ * "[WS2][Attention] H100 validation and reproduction guide for #235 PR1-PR8"
+ * (sections "Status": FP32 accumulation, fixed merge order, final-write
+ * downcast, no split-KV; "Acceptance": Out and attention-domain LSE,
+ * bitwise-equal results).
+ *
+ * Because every (query row, KV block) partial state is computed with the same
+ * operations wherever it is computed, and the fold over blocks always runs in
+ * ascending block index, the results are bit-identical across batch
+ * composition, chunk size, page placement, context-parallel split and the
+ * arrival order of partial states.
+ *
+ * Conventions (all entry points):
+ *  - Tensors are device pointers, caller-owned, contiguous, token-major:
+ *    q / out [batch][tokens][Hq][128], k / v [batch][tokens][Hkv][128],
+ *    lse [batch][tokens][Hq] (fp32, natural log).  bf16 tensors are passed as
+ *    raw 16-bit patterns.  Pointers marked [host] are host memory.
+ *  - head_dim must be 128; kv_block_size 64 or 128; Hq % Hkv == 0 with
+ *    Hq / Hkv in {1, 2, 4, 8}; acc_dtype must be RLA_DT_FP32.
+ *  - Every argument is validated on the host before anything is launched; a
+ *    rejected call writes nothing and returns an error code (no fallback).
+ *    rla_last_error() then describes the failure (thread-local).
+ *  - Work is enqueued on `hip_stream` (a hipStream_t, NULL = default stream)
+ *    and is asynchronous; device faults surface at the caller's synchronize.
+ *    A launch failure returns RLA_ERR_HIP.
+ *  - No call allocates device memory; scratch space is caller-provided.
+ *  - Thread safety: stateless apart from the thread-local error string.
+ *  - Empty rows (no visible key) give Out = 0 and LSE = -inf.
+ */
+#ifndef RLA_ATTN_H
+#define RLA_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  RLA_OK = 0,
+  RLA_ERR_NULL_POINTER = 1,
+  RLA_ERR_BAD_SHAPE = 2,
+  RLA_ERR_UNSUPPORTED = 3,
+  RLA_ERR_DUPLICATE_BLOCK = 4,
+  RLA_ERR_WORKSPACE_TOO_SMALL = 5,
+  RLA_ERR_HIP = 6
+} rla_status;
+
+typedef enum { RLA_DT_BF16 = 0, RLA_DT_FP32 = 1 } rla_dtype;
+
+/* Order in which partial states are folded.  GLOBAL_BLOCK_INDEX is the
+ * contract ("WS2 Attention PR5 Drift Benchmark", "Report Contract").  ARRIVAL
+ * folds in the order given and exists only as a diagnostic for
+ * rla_merge_states (it shows the drift that sorting removes); the attention
+ * entry points accept GLOBAL_BLOCK_INDEX only. */
+typedef enum { RLA_ORDER_GLOBAL_BLOCK_INDEX = 0, RLA_ORDER_ARRIVAL = 1 } rla_merge_order;
+
+/* Largest number of partial states one rla_merge_states call folds, and of
+ * blocks one emit-mode prefill call owns. */
+#define RLA_MAX_PARTS 512
+
+typedef struct {
+  int32_t num_q_heads;   /* local head shard: TP changes only these two counts  */
+  int32_t num_kv_heads;
+  int32_t head_dim;      /* must be 128                                          */
+  int32_t kv_block_size; /* 64 or 128 keys: the merge unit; block i holds keys
+                            [i*kv_block_size, (i+1)*kv_block_size) counted from
+                            sequence position 0                                  */
+  float softmax_scale;   /* applied in fp32 to the fp32 dot product              */
+  int32_t causal;        /* prefill/chunked: 1 = key position <= query position;
+                            decode: ignored (the query sees all cached keys)      */
+  int32_t merge_order;   /* rla_merge_order                                      */
+  int32_t acc_dtype;     /* must be RLA_DT_FP32                                  */
+  int32_t out_dtype;     /* RLA_DT_BF16 (downcast at final write) or RLA_DT_FP32 */
+} rla_attn_params;
+
+/* Partial states: the pages' state_i = (out_i, lse_i, global_block_index_i)
+ * for every row, one part per KV block ("Transformer Engine Reuse").
+ * out_i is normalised by the block's own sum; lse_i is that block's natural
+ * log-sum-exp; an empty block for a row is (0, -inf). */
+typedef struct {
+  float* out;                         /* [n_parts][rows][Hq][128] fp32, device */
+  float* lse;                         /* [n_parts][rows][Hq] fp32, device      */
+  const int64_t* global_block_index;  /* [host][n_parts], arrival order        */
+  int32_t n_parts;                    /* 1 .. RLA_MAX_PARTS                     */
+  int64_t rows;                       /* rows per part (batch * tokens)         */
+} rla_partials;
+
+/* Emulated context-parallel shard: a set of global KV blocks whose partial
+ * states are written instead of folded, for the query rows
+ * [q_begin, q_begin + q_count) of every sequence.  Part p of `partials`
+ * receives block kv_blocks[p] for rows b*q_count + (t - q_begin).  The caller
+ * sets partials->global_block_index (typically to kv_blocks) for the merge. */
+typedef struct {
+  const int64_t* kv_blocks;           /* [host][n_kv_blocks], distinct ids     */
+  int32_t n_kv_blocks;                /* 1 .. RLA_MAX_PARTS                     */
+  int64_t q_begin;                    /* query slab start (chunk-relative row)  */
+  int64_t q_count;                    /* query slab length                      */
+  rla_partials* partials;             /* out [n_kv_blocks][batch*q_count][Hq][128],
+                                         lse [n_kv_blocks][batch*q_count][Hq]  */
+} rla_shard;
+
+/* Full (causal) prefill over `batch` sequences of `seq_len` tokens.
+ * q [batch][seq_len][Hq][128], k, v [batch][seq_len][Hkv][128] bf16, post-RoPE.
+ * shard == NULL: fused path, writes out [batch][seq_len][Hq][128] (bf16 or fp32
+ * per out_dtype) and lse [batch][seq_len][Hq].  shard != NULL: emit path, writes
+ * the shard's partial states; out and lse are ignored (may be NULL). */
+rla_status rla_attn_prefill(const rla_attn_params* p, const void* q, const void* k, const void* v,
+                            int32_t batch, int32_t seq_len, const rla_shard* shard, void* out,
+                            float* lse, void* hip_stream);
+
+/* Chunked-prefill replay step ("Scope": chunked-prefill replay).  The chunk's
+ * query i sits at absolute position cache_len + i and attends the cached keys
+ * [0, cache_len + chunk_len) (causally); the chunk's own K/V must already be in
+ * the caches at positions [cache_len, cache_len + chunk_len).
+ * q_chunk [batch][chunk_len][Hq][128]; k_cache, v_cache [batch][s_max][Hkv][128];
+ * out [batch][chunk_len][Hq][128], lse [batch][chunk_len][Hq].
+ * Requires cache_len >= 0, chunk_len >= 1, cache_len + chunk_len <= s_max.
+ * shard as in rla_attn_prefill (q_begin/q_count relative to the chunk). */
+rla_status rla_attn_prefill_chunked(const rla_attn_params* p, const void* q_chunk, const void* k_cache,
+                                    const void* v_cache, int32_t batch, int32_t chunk_len,
+                                    int32_t cache_len, int32_t s_max, const rla_shard* shard, void* out,
+                                    float* lse, void* hip_stream);
+
+/* Paged-KV decode ("Commands": paged prefill/decode with batch and page-layout
+ * invariance): one query token per sequence attending its cached keys
+ * [0, context_lens[s]).  Key j of sequence s is slot j % page_size of page
+ * page_table[s][j / page_size] in the pools.
+ * q [batch][Hq][128]; k_pool, v_pool [num_pages][Hkv][page_size][128] bf16;
+ * page_table [batch][max_pages_per_seq] int32 (device); context_lens [batch]
+ * int32 (device).  host_context_lens [host][batch] may be NULL; when given the
+ * lengths are validated against max_context_len and the table width.
+ * page_size must divide kv_block_size.  Lengths above
+ * min(max_context_len, max_pages_per_seq*page_size) are clamped to it, and a
+ * page id outside [0, num_pages) is never dereferenced (its keys read as zero),
+ * so a bad table cannot fault, but its result is unspecified.
+ * workspace: at least rla_decode_workspace_bytes(p, batch, max_context_len)
+ * bytes of device memory (per-block partial states); contents on return are
+ * unspecified.  out [batch][Hq][128], lse [batch][Hq]. */
+rla_status rla_attn_decode_paged(const rla_attn_params* p, const void* q, const void* k_pool,
+                                 const void* v_pool, int64_t num_pages, int32_t page_size,
+                                 const int32_t* page_table, int32_t max_pages_per_seq,
+                                 const int32_t* context_lens, const int32_t* host_context_lens,
+                                 int32_t batch, int32_t max_context_len, void* workspace,
+                                 size_t workspace_bytes, void* out, float* lse, void* hip_stream);
+
+/* Merge of partial states ("Transformer Engine Reuse"; "Scope":
+ * merge_order_probe).  With RLA_ORDER_GLOBAL_BLOCK_INDEX the parts are folded
+ * in ascending global_block_index whatever their arrival order; a repeated
+ * index returns RLA_ERR_DUPLICATE_BLOCK.  Uses merge_order, out_dtype and
+ * num_q_heads of p.  out [rows][Hq][128] (bf16 or fp32), lse [rows][Hq]. */
+rla_status rla_merge_states(const rla_attn_params* p, const rla_partials* parts, void* out, float* lse,
+                            void* hip_stream);
+
+/* Workspace bytes rla_attn_decode_paged needs (0 on invalid arguments). */
+size_t rla_decode_workspace_bytes(const rla_attn_params* p, int32_t batch, int32_t max_context_len);
+
+/* Description of the last failure on the calling thread ("" after success). */
+const char* rla_last_error(void);
+
+/* Provenance string naming the arithmetic contract, e.g. "rla.attention.core.v1". */
+const char* rla_core_id(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RLA_ATTN_H */

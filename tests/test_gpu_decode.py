@@ -1,0 +1,118 @@
+"""GPU paged-KV decode: parity with the FP64 oracle, and bitwise invariance to
+batch composition (a sequence alone vs in the batch) and to page placement
+(pages relocated in the pool).  Also: decode equals the last row of a prefill
+over the same tokens, bit for bit, because both run the same per-block core.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from deterministic_gqa_attention_amd import api
+from deterministic_gqa_attention_amd import inputs as gen
+from tests.gpu_util import assert_bitwise, check_parity, dev_bf16, dev_i32, host_f64, say
+
+pytestmark = pytest.mark.gpu
+
+SMALL = gen.DecodeConfig(41, "small paged decode", batch=7, Hq=8, Hkv=2, D=128, page_size=16, num_pages=512,
+                         len_lo=1, len_hi=700, block=128)
+SMALL_LENS = np.array([1, 16, 127, 128, 129, 300, 700], np.int32)
+
+
+def _decode(d, cfg, *, block, out_dtype=torch.bfloat16, max_ctx=None, seqs=None):
+    """Run decode on the inputs in d (numpy); the pools are uploaded once and
+    cached in d under "_dev"."""
+    if "_dev" not in d:
+        d["_dev"] = (dev_bf16(d["k_pool"]), dev_bf16(d["v_pool"]))
+    kp, vp = d["_dev"]
+    lens = d["ctx_lens"] if seqs is None else d["ctx_lens"][seqs]
+    table = d["page_table"] if seqs is None else d["page_table"][seqs]
+    q = d["q"] if seqs is None else d["q"][seqs]
+    max_ctx = int(cfg.len_hi) if max_ctx is None else max_ctx
+    return api.decode_paged(dev_bf16(q), kp, vp, dev_i32(table), dev_i32(lens), block=block,
+                            max_context_len=max_ctx, host_ctx_lens=lens, out_dtype=out_dtype)
+
+
+@pytest.mark.parametrize("block", [64, 128])
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])
+def test_small_decode_parity(block, out_dtype):
+    d = gen.decode_inputs(SMALL, lengths=SMALL_LENS)
+    say(f"[decode] small parity block={block} out={out_dtype}")
+    out, lse = _decode(d, SMALL, block=block, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    ro, rl = oracle.decode_paged(d["q"], d["k_pool"], d["v_pool"], d["page_table"], d["ctx_lens"],
+                                 scale=SMALL.softmax_scale)
+    stats = check_parity(host_f64(out), host_f64(lse), ro, rl, f32_out=out_dtype == torch.float32,
+                         what="small decode")
+    say(f"    parity {stats}")
+
+
+def test_small_decode_batch_and_relocation():
+    d = gen.decode_inputs(SMALL, lengths=SMALL_LENS)
+    say("[decode] small batch/relocation invariance")
+    bo, bl = _decode(d, SMALL, block=128)
+    for s in (0, 3, 6):
+        so, sl = _decode(d, SMALL, block=128, seqs=[s])
+        assert_bitwise(so[0], bo[s], f"seq {s} alone Out")
+        assert_bitwise(sl[0], bl[s], f"seq {s} alone LSE")
+    r = gen.relocate({k: d[k] for k in ("q", "k_pool", "v_pool", "page_table", "ctx_lens")},
+                     gen.relocation(SMALL, SMALL.num_pages))
+    ro, rl = _decode(r, SMALL, block=128)
+    assert_bitwise(ro, bo, "relocated Out")
+    assert_bitwise(rl, bl, "relocated LSE")
+
+
+def test_decode_equals_prefill_last_row():
+    """Same per-(row, block) arithmetic: decode over a cache of L tokens equals
+    row L-1 of causal prefill over the same tokens, bitwise."""
+    d = gen.decode_inputs(SMALL, lengths=SMALL_LENS)
+    say("[decode] decode == prefill last row")
+    do, dl = _decode(d, SMALL, block=128, out_dtype=torch.float32)
+    P = SMALL.page_size
+    for s in (2, 4, 6):
+        L = int(SMALL_LENS[s])
+        pages = d["page_table"][s, : -(-L // P)]
+        k = d["k_pool"][pages].transpose(0, 2, 1, 3).reshape(-1, SMALL.Hkv, 128)[:L][None]
+        v = d["v_pool"][pages].transpose(0, 2, 1, 3).reshape(-1, SMALL.Hkv, 128)[:L][None]
+        q = np.zeros((1, L, SMALL.Hq, 128), np.uint16)
+        q[0, L - 1] = d["q"][s]
+        po, pl = api.prefill(dev_bf16(q), dev_bf16(k), dev_bf16(v), block=128, out_dtype=torch.float32)
+        assert_bitwise(do[s], po[0, L - 1], f"seq {s} Out")
+        assert_bitwise(dl[s], pl[0, L - 1], f"seq {s} LSE")
+
+
+def test_empty_context():
+    d = gen.decode_inputs(SMALL, lengths=np.array([0, 5, 0], np.int32))
+    say("[decode] zero-length contexts")
+    out, lse = _decode(d, SMALL, block=128, out_dtype=torch.float32)
+    assert torch.all(out[0] == 0) and torch.all(out[2] == 0)
+    assert torch.all(torch.isneginf(lse[0])) and torch.all(torch.isneginf(lse[2]))
+    assert torch.isfinite(lse[1]).all()
+
+
+@pytest.mark.slow
+def test_paged_decode_64_seqs_full():
+    """64 sequences, lengths U[512, 16384], page size 16, 1M-slot pool, random
+    page table: parity for every sequence; one sequence alone == in the batch;
+    relocated pages give identical bits."""
+    cfg = gen.CFG4
+    d = gen.decode_inputs(cfg)
+    say("[decode] 64 seqs full")
+    out, lse = _decode(d, cfg, block=cfg.block)
+    torch.cuda.synchronize()
+    ro, rl = oracle.decode_paged(d["q"], d["k_pool"], d["v_pool"], d["page_table"], d["ctx_lens"],
+                                 scale=cfg.softmax_scale)
+    stats = check_parity(host_f64(out), host_f64(lse), ro, rl, f32_out=False, what="64-seq decode")
+    say(f"    parity {stats}")
+    for s in (0, 17, 63):
+        so, sl = _decode(d, cfg, block=cfg.block, seqs=[s])
+        assert_bitwise(so[0], out[s], f"seq {s} alone Out")
+        assert_bitwise(sl[0], lse[s], f"seq {s} alone LSE")
+    say("[decode] 64 seqs relocated")
+    r = gen.relocate({k: d[k] for k in ("q", "k_pool", "v_pool", "page_table", "ctx_lens")},
+                     gen.relocation(cfg, cfg.num_pages))
+    del d
+    torch.cuda.empty_cache()
+    o2, l2 = _decode(r, cfg, block=cfg.block)
+    assert_bitwise(o2, out, "relocated Out")
+    assert_bitwise(l2, lse, "relocated LSE")

@@ -13,6 +13,10 @@ def test_bf16_rounding_matches_torch_rne():
     f32 = x.astype(np.float32)
     ref = torch.from_numpy(f32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     assert np.array_equal(gen.f64_to_bf16_bits(x), ref)
+    assert np.array_equal(gen.f64_to_bf16_bits_reference(x), ref)
+    nan = np.array([np.nan, -np.nan])
+    assert (gen.f64_to_bf16_bits_reference(nan) & 0x7FC0 == 0x7FC0).all()
+    assert (gen.f64_to_bf16_bits(nan) & 0x7F80 == 0x7F80).all() and (gen.f64_to_bf16_bits(nan) & 0x7F).any()
     # ties round to even: 1 + 2^-8 sits halfway between 1 and 1 + 2^-7
     assert gen.f64_to_bf16_bits(np.array([1.0 + 2.0 ** -8]))[0] == 0x3F80
     assert gen.f64_to_bf16_bits(np.array([1.0 + 3 * 2.0 ** -8]))[0] == 0x3F82

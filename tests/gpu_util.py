@@ -47,7 +47,8 @@ def check_parity(out_g, lse_g, out_o, lse_o, *, f32_out: bool, what: str):
     assert not bad.any(), (f"{what}: {int(bad.sum())} Out elements exceed {bound}; "
                            f"max abs err {err.max():.3e}")
     both_inf = np.isneginf(lg) & np.isneginf(lse_o)
-    lerr = np.where(both_inf, 0.0, np.abs(lg - lse_o))
+    with np.errstate(invalid="ignore"):
+        lerr = np.where(both_inf, 0.0, np.abs(lg - lse_o))
     assert not np.isnan(lerr).any(), f"{what}: NaN / mismatched -inf in LSE"
     assert lerr.max(initial=0.0) <= LSE_ATOL, f"{what}: LSE max abs err {lerr.max():.3e} > {LSE_ATOL}"
     denom = np.maximum(np.abs(out_o), 1e-6)

@@ -77,6 +77,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--only", choices=["prefill", "decode", "copy"], default=None,
+                    help="run one leg only (for profiler and counter runs)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -84,17 +86,23 @@ def main():
               "the attention path runs on a single device and nothing is sharded across GPUs.", file=sys.stderr)
         sys.exit(2)
 
+    if args.only == "copy":
+        copy_calibration(args)
+        return
+    if args.only == "decode":
+        args.no_cpu_baseline = True
+
     cfg = gen.CFG2
     log("generating prefill inputs")
     q, k, v = gen.prefill_inputs(cfg)
     dcfg = gen.CFG4
     d = None
-    if not args.no_decode:
+    if not args.no_decode and args.only != "prefill":
         log("generating paged-decode inputs")
         d = gen.decode_inputs(dcfg)
 
     base = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.only is None:
         log(f"timing the CPU oracle for ~{args.cpu_seconds:.0f} s")
         base = cpu_baseline(q, k, v, cfg, args.cpu_seconds)
         log(f"cpu baseline {base['value'] * 1e3:.2f} GFLOP/s on {base['cores']} threads")
@@ -112,8 +120,10 @@ def main():
     stream = torch.cuda.current_stream(dev)
     flops = cfg.flops()
 
+    if args.only == "decode":
+        args.steps = 0
     log("prefill warmup")
-    for _ in range(args.warmup):
+    for _ in range(args.warmup if args.steps else 0):
         api.prefill(qd, kd, vd, block=cfg.block)
     torch.cuda.synchronize()
 
@@ -131,15 +141,53 @@ def main():
         ends[i].record(stream)
     t_end.record(stream)
     torch.cuda.synchronize()
-    total_ms = t_begin.elapsed_time(t_end)
-    launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    ms_per_step = total_ms / args.steps
-    kern_ms = float(np.mean(launch_ms))
-    tflops = flops / (ms_per_step * 1e-3) / 1e12
-    achieved = flops / (kern_ms * 1e-3) / 1e12
-    log(f"prefill {ms_per_step:.3f} ms/step, kernel {kern_ms:.3f} ms, {tflops:.1f} TFLOP/s")
+    if args.steps:
+        total_ms = t_begin.elapsed_time(t_end)
+        launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+        ms_per_step = total_ms / args.steps
+        kern_ms = float(np.mean(launch_ms))
+        tflops = flops / (ms_per_step * 1e-3) / 1e12
+        achieved = flops / (kern_ms * 1e-3) / 1e12
+        log(f"prefill {ms_per_step:.3f} ms/step, kernel {kern_ms:.3f} ms, {tflops:.1f} TFLOP/s")
+    else:
+        total_ms = ms_per_step = kern_ms = tflops = achieved = float("nan")
+    if args.only == "prefill":
+        print(json.dumps({"only": "prefill", "ms_per_step": ms_per_step, "kernel_ms": kern_ms, "tflops": tflops}))
+        return
 
-    # invariance spot checks (untimed): max abs drift must be 0.0
+    drift_batch = drift_cp = None
+    if args.only is None:
+        drift_batch, drift_cp = invariance_probe(api, cfg, qd, kd, vd, out, dev)
+        log(f"invariance drift: batch {drift_batch}, CP=2 reversed {drift_cp}")
+    del qd, kd, vd, out
+    torch.cuda.empty_cache()
+    decode = decode_leg(args, api, d, dcfg, up, dev, stream) if d is not None else None
+    if args.only == "decode":
+        print(json.dumps({"only": "decode", "decode": decode}))
+        return
+
+    line = {
+        "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "fused causal prefill B=4 S=4096 Hq=32 Hkv=8 D=128, 128-key blocks, bf16 in/out, "
+                               "fp32 accumulate", "global_batch": cfg.B, "seq_len": cfg.S, "parallelism": "none",
+                   "flop_per_step": flops},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel_ms": round(kern_ms, 4)},
+        "decode": decode,
+        "invariance": {"batch_alone_vs_batch": drift_batch, "cp2_reversed_arrival": drift_cp},
+        "cpu_baseline": base,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def invariance_probe(api, cfg, qd, kd, vd, out, dev):
+    """Untimed: a sequence alone vs in the batch, and CP=2 emit+merge with
+    reversed arrival on the last 512 query rows; returns the max abs drifts."""
+    import torch
+
     fo, fl = out
     so, sl = api.prefill(qd[1:2].contiguous(), kd[1:2].contiguous(), vd[1:2].contiguous(), block=cfg.block)
     drift_batch = max((so[0].float() - fo[1].float()).abs().max().item(),
@@ -158,63 +206,74 @@ def main():
     drift_cp = max((mo.float() - fo[:, q0:].float()).abs().max().item(), (ml - fl[:, q0:]).abs().max().item())
     del po, pl
     torch.cuda.empty_cache()
-    log(f"invariance drift: batch {drift_batch}, CP=2 reversed {drift_cp}")
+    return drift_batch, drift_cp
 
-    decode = None
-    if d is not None:
-        log("decode setup")
-        kp, vp = up(d["k_pool"]), up(d["v_pool"])
-        qq = up(d["q"])
-        table = torch.from_numpy(d["page_table"]).to(dev)
-        lens = torch.from_numpy(d["ctx_lens"]).to(dev)
-        host_lens = d["ctx_lens"]
-        max_ctx = dcfg.len_hi
-        ws = torch.empty((api.decode_workspace_bytes(dcfg.Hq, dcfg.Hkv, dcfg.batch, max_ctx, block=dcfg.block),),
-                         dtype=torch.uint8, device=dev)
-        flush = torch.empty((1 << 30,), dtype=torch.uint8, device=dev)  # > 256 MB last-level cache
-        kv_bytes = gen.decode_kv_bytes(host_lens, dcfg.Hkv, dcfg.D)
-        used_pages = int((-(-host_lens.astype(np.int64) // dcfg.page_size)).sum())
-        other = dcfg.batch * dcfg.Hq * dcfg.D * 2 * 2 + dcfg.batch * dcfg.Hq * 4 + used_pages * 4 + dcfg.batch * 4
-        alg_bytes = kv_bytes + other
-        for _ in range(2):
-            api.decode_paged(qq, kp, vp, table, lens, block=dcfg.block, max_context_len=max_ctx,
-                             host_ctx_lens=host_lens, workspace=ws)
-        times = []
-        for _ in range(args.decode_steps):
-            flush.fill_(1)
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            api.decode_paged(qq, kp, vp, table, lens, block=dcfg.block, max_context_len=max_ctx,
-                             host_ctx_lens=host_lens, workspace=ws)
-            e1.record(stream)
-            torch.cuda.synchronize()
-            times.append(e0.elapsed_time(e1))
-        dms = float(np.median(times))
-        gbs = kv_bytes / (dms * 1e-3) / 1e9
-        ach = alg_bytes / (dms * 1e-3) / 1e9
-        decode = {"value": round(gbs, 1), "unit": "GB/s", "ms": round(dms, 4), "kv_bytes": kv_bytes,
-                  "workload": "paged decode, 64 seqs, len U[512,16384] (sum %d), Hq=32 Hkv=8 D=128, page 16, "
-                              "1M-slot pool, 128-key blocks, bf16 out" % int(host_lens.sum()),
-                  "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                               "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None}}
-        log(f"decode {dms:.3f} ms, {gbs:.0f} GB/s KV")
 
-    line = {
-        "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": "fused causal prefill B=4 S=4096 Hq=32 Hkv=8 D=128, 128-key blocks, bf16 in/out, "
-                               "fp32 accumulate", "global_batch": cfg.B, "seq_len": cfg.S, "parallelism": "none",
-                   "flop_per_step": flops},
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                     "kernel_ms": round(kern_ms, 4)},
-        "decode": decode,
-        "invariance": {"batch_alone_vs_batch": drift_batch, "cp2_reversed_arrival": drift_cp},
-        "cpu_baseline": base,
-    }
-    print(json.dumps(line), flush=True)
+def decode_leg(args, api, d, dcfg, up, dev, stream):
+    """Paged decode over the 64-sequence workload; caches flushed before each
+    timed repetition.  Returns the decode record of the JSON line."""
+    import torch
+
+    log("decode setup")
+    kp, vp = up(d["k_pool"]), up(d["v_pool"])
+    qq = up(d["q"])
+    table = torch.from_numpy(d["page_table"]).to(dev)
+    lens = torch.from_numpy(d["ctx_lens"]).to(dev)
+    host_lens = d["ctx_lens"]
+    max_ctx = dcfg.len_hi
+    ws = torch.empty((api.decode_workspace_bytes(dcfg.Hq, dcfg.Hkv, dcfg.batch, max_ctx, block=dcfg.block),),
+                     dtype=torch.uint8, device=dev)
+    flush = torch.empty((1 << 30,), dtype=torch.uint8, device=dev)  # > 256 MB last-level cache
+    kv_bytes = gen.decode_kv_bytes(host_lens, dcfg.Hkv, dcfg.D)
+    used_pages = int((-(-host_lens.astype(np.int64) // dcfg.page_size)).sum())
+    other = dcfg.batch * dcfg.Hq * dcfg.D * 2 * 2 + dcfg.batch * dcfg.Hq * 4 + used_pages * 4 + dcfg.batch * 4
+    alg_bytes = kv_bytes + other
+    for _ in range(2):
+        api.decode_paged(qq, kp, vp, table, lens, block=dcfg.block, max_context_len=max_ctx,
+                         host_ctx_lens=host_lens, workspace=ws)
+    times = []
+    for _ in range(args.decode_steps):
+        flush.fill_(1)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        api.decode_paged(qq, kp, vp, table, lens, block=dcfg.block, max_context_len=max_ctx,
+                         host_ctx_lens=host_lens, workspace=ws)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    dms = float(np.median(times))
+    gbs = kv_bytes / (dms * 1e-3) / 1e9
+    ach = alg_bytes / (dms * 1e-3) / 1e9
+    decode = {"value": round(gbs, 1), "unit": "GB/s", "ms": round(dms, 4), "kv_bytes": kv_bytes,
+              "workload": "paged decode, 64 seqs, len U[512,16384] (sum %d), Hq=32 Hkv=8 D=128, page 16, "
+                          "1M-slot pool, 128-key blocks, bf16 out" % int(host_lens.sum()),
+              "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                           "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None}}
+    log(f"decode {dms:.3f} ms, {gbs:.0f} GB/s KV")
+    return decode
+
+
+def copy_calibration(args):
+    """A plain device copy of known size (1 GiB read + 1 GiB written per
+    dispatch), used to scale the FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+
+    n = 1 << 30
+    src = torch.ones((n,), dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(max(1, args.warmup)):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(max(1, args.steps)):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / max(1, args.steps)
+    print(json.dumps({"only": "copy", "bytes_read": n, "bytes_written": n, "ms": ms,
+                      "GBps": 2 * n / (ms * 1e-3) / 1e9}))
 
 
 if __name__ == "__main__":

@@ -92,10 +92,7 @@ rla_status prefill_common(const rla_attn_params* p, const void* q, const void* k
   a.B = batch;
   a.Hq = Hq;
   a.Hkv = Hkv;
-  a.G = g;
-  a.heads_per_wg = std::min(g, 4);
-  a.pos_groups = 4 / a.heads_per_wg;
-  a.hsubs = g / a.heads_per_wg;
+  a.G = g;  // the launcher picks the tile shape (heads_per_wg, pos_groups, hsubs, n_ptiles)
   a.causal = p->causal;
   a.c = score_scale(p);
 
@@ -140,8 +137,6 @@ rla_status prefill_common(const rla_attn_params* p, const void* q, const void* k
   a.q = static_cast<const uint16_t*>(q) + q_begin * Hq * D;
   a.Sq = static_cast<int32_t>(q_count);
   a.pos0 = pos0 + q_begin;
-  const int tile_rows = 32 * a.pos_groups;
-  a.n_ptiles = static_cast<int32_t>((q_count + tile_rows - 1) / tile_rows);
   hipError_t e = rla::launch_prefill(a, p->kv_block_size, p->out_dtype == RLA_DT_FP32, emit,
                                      static_cast<hipStream_t>(stream));
   return hip_status(e, "prefill launch");

@@ -13,10 +13,11 @@
 //
 // The contract, per query row q and KV block b (keys [b*Bk, (b+1)*Bk) counted
 // from sequence position 0):
-//   dot_j = MFMA bf16 chain over D in 8 fixed 16-wide steps, FP32 accumulate
-//   t_j   = dot_j * c  with c = fl32(scale * log2 e); masked keys -> -inf (select)
-//   m_t   = max_j t_j (exact)
-//   p_j   = 2^(t_j - m_t)                       (v_exp_f32)
+//   dot_j = MFMA bf16 chain over D in 8 fixed 16-wide steps, FP32 accumulate;
+//           masked keys -> -inf (select)
+//   m_t   = fl(max_j dot_j * c) with c = fl32(scale * log2 e)  (block max in
+//           the log2 domain; equal to max_j fl(dot_j * c) since c > 0)
+//   p_j   = 2^fma(dot_j, c, -m_t)                (v_exp_f32)
 //   l_b   = fixed tree over the 16 values a lane holds per 32-key sub-tile,
 //           plus its partner lane, then a fixed tree over the sub-tiles
 //   acc_b = MFMA chain over the block's keys from zero, P rounded to bf16
@@ -56,6 +57,16 @@ __device__ __forceinline__ float hw_exp2(float x) { return __builtin_amdgcn_exp2
 __device__ __forceinline__ float hw_log2(float x) { return __builtin_amdgcn_logf(x); }
 // e^x as used by the fold: one rounding for the scaling, then v_exp_f32.
 __device__ __forceinline__ float fold_exp(float x) { return hw_exp2(x * kLog2e); }
+
+// Block max in the log2 domain from the max raw dot (-inf when the row has no
+// visible key in the block), and the offset used by the exponentials (0 for
+// an empty row, so masked scores give exactly 0 instead of NaN).
+__device__ __forceinline__ float block_m(float max_dot, float c) {
+  return max_dot == kNegInf ? kNegInf : max_dot * c;
+}
+__device__ __forceinline__ float block_m_use(float m_t) { return m_t == kNegInf ? 0.0f : m_t; }
+// Unnormalised probability of a (masked-to--inf) raw dot.
+__device__ __forceinline__ float block_p(float dot, float c, float m_use) { return hw_exp2(fmaf(dot, c, -m_use)); }
 
 // v_mfma_f32_32x32x16_bf16.  A is 32 (rows) x 16 (k), B is 16 (k) x 32 (cols).
 // Lane l supplies A row l%32 and B column l%32, k values 8*(l/32)+0..7 of the

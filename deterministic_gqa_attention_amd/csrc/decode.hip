@@ -4,11 +4,13 @@
 // of each row in ascending block index.
 //
 // Keys are gathered through the page table: key j of sequence s is slot j % P
-// of page page_table[s][j / P] in a pool laid out [page][kv head][slot][dim].
-// The per-(row, block) arithmetic is the same as in the prefill kernel (same
-// MFMA shape and operand order, same softmax tree, same PV chain), only split
-// over the four waves: wave w computes score sub-tile w and output dim tile w,
-// and the block max, sub-tile sums and bf16 P go through LDS.  Rows are the
+// of page page_table[s][j / P] in a pool laid out [page][kv head][slot][dim];
+// the workgroup stages the block in LDS with direct global->LDS loads whose
+// per-lane source addresses do the gather.  The per-(row, block) arithmetic is
+// the same as in the prefill kernel (same LDS layout and fragments, same MFMA
+// shape and operand order, same softmax tree, same PV chain), only split over
+// the four waves: wave w computes score sub-tile w and output dim tile w, and
+// the block max, sub-tile sums and bf16 P go through LDS.  Rows are the
 // group's q heads for the one query token (columns >= G are zero padding).
 #include "kernels.hpp"
 #include "tile.hpp"
@@ -22,9 +24,8 @@ constexpr int kThreads = 256;
 template <int BK, bool F32>
 struct DecodeLds {
   static constexpr int NKT = BK / 32;
-  static constexpr int kV = TileLayout<BK>::kVBytes;
   static constexpr int kPBytesPerTile = 64 * 32 * (F32 ? 2 : 1);  // 64 lanes x 16 bf16 (x2 hi/lo)
-  static constexpr int kPOff = kV;
+  static constexpr int kPOff = TileLayout<BK>::kBytes;
   static constexpr int kMaxOff = kPOff + NKT * kPBytesPerTile;
   static constexpr int kSumOff = kMaxOff + NKT * 32 * 4;
   static constexpr int kBytes = kSumOff + NKT * 32 * 4;
@@ -39,12 +40,34 @@ __device__ __forceinline__ int64_t page_row_off(const DecodeArgs& a, int seq, in
   return ((static_cast<int64_t>(ok ? page : 0) * a.Hkv + hk) * a.P + key % a.P) * kHeadDim;
 }
 
+// Direct global->LDS loads of one KV block gathered through the page table,
+// in the layout of TileLayout (rows past len load key len-1: masked).
+template <int BK>
+__device__ __forceinline__ void issue_paged_loads(char* buf, const DecodeArgs& a, int seq, int hk, int64_t key0,
+                                                  int64_t len) {
+  using L = TileLayout<BK>;
+  constexpr int NW = kThreads / 64;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  const int lane = threadIdx.x & 63;
+  const int p = lane & 15;
+#pragma unroll
+  for (int i = 0; i < L::kLoadsPerRegion / NW; ++i) {
+    const int n = wave + NW * i;
+    const int r = 4 * n + (lane >> 4);
+    int64_t key = key0 + r;
+    key = key < len ? key : len - 1;
+    bool ok;
+    const int64_t off = page_row_off(a, seq, hk, key, ok);  // ok == false: page 0 row (masked or caller error)
+    direct_load16(a.k_pool + off + ((p ^ L::k_swz(r)) << 3), buf + n * 1024);
+    direct_load16(a.v_pool + off + ((p ^ L::v_swz(r)) << 3), buf + L::kKBytes + n * 1024);
+  }
+}
+
 template <int BK, bool F32>
 __global__ __launch_bounds__(kThreads) void decode_items_kernel(const DecodeArgs a) {
   using Lay = DecodeLds<BK, F32>;
   constexpr int NKT = Lay::NKT;
   __shared__ __attribute__((aligned(16))) char lds[Lay::kBytes];
-  char* lv = lds;
   char* lp = lds + Lay::kPOff;
   float* red_max = reinterpret_cast<float*>(lds + Lay::kMaxOff);
   float* red_sum = reinterpret_cast<float*>(lds + Lay::kSumOff);
@@ -65,77 +88,46 @@ __global__ __launch_bounds__(kThreads) void decode_items_kernel(const DecodeArgs
   const int col = lane & 31;
   const int half = lane >> 5;
 
-  // ---- stage V^T for the block (all threads), gathered through the page table
+  issue_paged_loads<BK>(lds, a, seq, hk, key0, len);
+
+  // Q fragments of the group's heads (columns >= G are zero)
+  bf16x8 qf[kDSteps];
   {
-    constexpr int VIT = BK / 64;
-    const int dc = tid & 15;
-    const int kg0 = tid >> 4;
-    u32x4 vx[VIT][4];
+    const bool qok = col < a.G;
+    const uint16_t* qrow = a.q + (static_cast<int64_t>(seq) * a.Hq + hk * a.G + (qok ? col : 0)) * kHeadDim + 8 * half;
 #pragma unroll
-    for (int i = 0; i < VIT; ++i) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int64_t key = key0 + 4 * (kg0 + 16 * i) + j;
-        vx[i][j] = u32x4{0, 0, 0, 0};
-        if (key < len) {
-          bool ok;
-          const int64_t off = page_row_off(a, seq, hk, key, ok);
-          if (ok) vx[i][j] = gload16(a.v_pool + off + dc * 8);
-        }
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < VIT; ++i) {
-      u32x2 tt[8];
-      transpose4x8(vx[i], tt);
-      const int kg = kg0 + 16 * i;
-#pragma unroll
-      for (int ii = 0; ii < 8; ++ii) lds_store8(lv, TileLayout<BK>::v_off(8 * dc + ii, kg), tt[ii]);
-    }
+    for (int ds = 0; ds < kDSteps; ++ds) qf[ds] = as_bf16x8(qok ? gload16(qrow + 16 * ds) : u32x4{0, 0, 0, 0});
   }
+  wait_direct_loads();
+  __syncthreads();
 
   // ---- scores of sub-tile kt = wave (waves < NKT)
   f32x16 s = f32x16{};
-  float m_lane = kNegInf;
   if (wave < NKT) {
-    bf16x8 kf[kDSteps];
-    bf16x8 qf[kDSteps];
-    const int64_t key = key0 + wave * 32 + col;
-    bool kok = false;
-    int64_t koff = 0;
-    if (key < len) {
-      koff = page_row_off(a, seq, hk, key, kok);
-    }
-    const bool qok = col < a.G;
-    const uint16_t* qrow = a.q + (static_cast<int64_t>(seq) * a.Hq + hk * a.G + col) * kHeadDim + 8 * half;
 #pragma unroll
-    for (int ds = 0; ds < kDSteps; ++ds) {
-      kf[ds] = as_bf16x8(kok ? gload16(a.k_pool + koff + 16 * ds + 8 * half) : u32x4{0, 0, 0, 0});
-      qf[ds] = as_bf16x8(qok ? gload16(qrow + 16 * ds) : u32x4{0, 0, 0, 0});
-    }
-#pragma unroll
-    for (int ds = 0; ds < kDSteps; ++ds) s = mfma(kf[ds], qf[ds], s);
+    for (int ds = 0; ds < kDSteps; ++ds) s = mfma(k_frag<BK>(lds, wave, ds, col, half), qf[ds], s);
+    float m_lane = kNegInf;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int64_t kk = key0 + wave * 32 + acc_row(v, half);
-      float t = s[v] * a.c;
-      t = kk < len ? t : kNegInf;
-      s[v] = t;
-      m_lane = fmaxf(m_lane, t);
+      const float d = kk < len ? s[v] : kNegInf;
+      s[v] = d;
+      m_lane = fmaxf(m_lane, d);
     }
     m_lane = fmaxf(m_lane, partner(m_lane));
     if (half == 0) red_max[wave * 32 + col] = m_lane;
   }
   __syncthreads();
 
-  float m_t = red_max[col];
+  float mx = red_max[col];
 #pragma unroll
-  for (int kt = 1; kt < NKT; ++kt) m_t = fmaxf(m_t, red_max[kt * 32 + col]);
-  const float m_use = (m_t == kNegInf) ? 0.0f : m_t;
+  for (int kt = 1; kt < NKT; ++kt) mx = fmaxf(mx, red_max[kt * 32 + col]);
+  const float m_t = block_m(mx, a.c);
+  const float m_use = block_m_use(m_t);
 
   if (wave < NKT) {
 #pragma unroll
-    for (int v = 0; v < 16; ++v) s[v] = hw_exp2(s[v] - m_use);
+    for (int v = 0; v < 16; ++v) s[v] = block_p(s[v], a.c, m_use);
     const float aa = tree16(s);
     const float sum = aa + partner(aa);
     if (half == 0) red_sum[wave * 32 + col] = sum;
@@ -148,19 +140,15 @@ __global__ __launch_bounds__(kThreads) void decode_items_kernel(const DecodeArgs
         const float p1 = s[8 * st + 2 * w + 1];
         const uint32_t h = pack_bf16(p0, p1);
         ph[st][w] = h;
-        if constexpr (F32) {
-          const float r0 = p0 - bf16_lo_to_f32(h);
-          const float r1 = p1 - bf16_hi_to_f32(h);
-          pl[st][w] = pack_bf16(r0, r1);
-        }
+        if constexpr (F32) pl[st][w] = pack_bf16(p0 - bf16_lo_to_f32(h), p1 - bf16_hi_to_f32(h));
       }
     }
     char* my = lp + wave * Lay::kPBytesPerTile + lane * (F32 ? 64 : 32);
-    lds_store16(my, 0, ph[0]);
-    lds_store16(my, 16, ph[1]);
+    *reinterpret_cast<u32x4*>(my) = ph[0];
+    *reinterpret_cast<u32x4*>(my + 16) = ph[1];
     if constexpr (F32) {
-      lds_store16(my, 32, pl[0]);
-      lds_store16(my, 48, pl[1]);
+      *reinterpret_cast<u32x4*>(my + 32) = pl[0];
+      *reinterpret_cast<u32x4*>(my + 48) = pl[1];
     }
   }
   __syncthreads();
@@ -178,7 +166,7 @@ __global__ __launch_bounds__(kThreads) void decode_items_kernel(const DecodeArgs
     const char* pp = lp + kt * Lay::kPBytesPerTile + lane * (F32 ? 64 : 32);
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
-      const bf16x8 vf = v_frag<BK>(lv, dt, kt, st, col, half);
+      const bf16x8 vf = v_frag<BK>(lds, dt, kt, st);
       acc = mfma(vf, as_bf16x8(lds_load16(pp, 16 * st)), acc);
       if constexpr (F32) acc = mfma(vf, as_bf16x8(lds_load16(pp, 32 + 16 * st)), acc);
     }

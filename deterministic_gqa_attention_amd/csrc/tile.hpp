@@ -1,15 +1,17 @@
-// LDS layouts of one staged KV block (Bk keys x 128 dims, bf16) and the
-// register transposition used to build the V^T layout.
+// LDS layout of one staged KV block (Bk keys x 128 dims, bf16) and the
+// fragment reads of it.
 //
-// K is kept key-major, one 256-byte row per key, with its 16-byte chunks
-// XOR-swizzled by the low 3 bits of the key so that the 32 rows an MFMA
-// A-fragment read touches fall in distinct bank groups.
-//
-// V is kept transposed (dimension-major, keys contiguous) because the PV
-// product contracts over keys: an A-fragment lane needs 8 keys of one
-// dimension.  8-byte units (4 keys) are XOR-swizzled by f(d) below, which
-// keeps both the transposing writes and the fragment reads free of bank
-// conflicts.
+// Both K and V are kept key-major, one 256-byte row per key, filled straight
+// from global memory by global_load_lds_dwordx4 (each wave instruction writes
+// 1 KiB = 4 rows; the lane -> global address map applies the swizzle, so the
+// LDS side is a plain contiguous write).  The 16-byte chunks of a row are
+// XOR-swizzled:
+//  * K rows by the low 4 bits of the key, so the 16 rows an MFMA A-fragment
+//    read (ds_read_b128) touches per cycle land in 16 distinct bank groups;
+//  * V rows by fV(r) = ((r & 3) << 2) ^ ((r >> 2) & 3), so the transposed
+//    reads (ds_read_b64_tr_b16: four lanes read one 16-dim row segment of a
+//    key, lane i of the 16-lane group receives dim i of four keys) of 4 keys
+//    x 4 chunks hit 32 distinct bank pairs.
 #pragma once
 
 #include "core.hpp"
@@ -21,69 +23,93 @@ struct TileLayout {
   static constexpr int kKBytes = BK * kHeadDim * 2;
   static constexpr int kVBytes = BK * kHeadDim * 2;
   static constexpr int kBytes = kKBytes + kVBytes;
-  static constexpr int kVRowBytes = BK * 2;
+  static constexpr int kLoadsPerRegion = BK / 4;  // 1 KiB direct loads per region
 
-  // byte offset of 16-byte chunk c (dims 8c..8c+7) of key row r
-  __device__ static __forceinline__ int k_off(int r, int c) { return r * 256 + ((c ^ (r & 7)) << 4); }
-
-  __device__ static __forceinline__ int v_swz(int d) { return (d & 15) ^ ((d >> 4) & 7); }
-  // byte offset, within the V^T region, of 8-byte unit u (keys 4u..4u+3) of
-  // dimension row d
-  __device__ static __forceinline__ int v_off(int d, int u) {
-    return d * kVRowBytes + ((u ^ v_swz(d)) << 3);
-  }
+  __device__ static __forceinline__ int k_swz(int r) { return r & 15; }
+  __device__ static __forceinline__ int v_swz(int r) { return ((r & 3) << 2) ^ ((r >> 2) & 3); }
+  // byte offset of logical 16-byte chunk c (dims 8c..8c+7) of key row r
+  __device__ static __forceinline__ int k_off(int r, int c) { return r * 256 + ((c ^ k_swz(r)) << 4); }
+  __device__ static __forceinline__ int v_off(int r, int c) { return kKBytes + r * 256 + ((c ^ v_swz(r)) << 4); }
 };
 
-// Transpose a 4-key x 8-dim bf16 sub-block: r[j] holds dims 8dc..8dc+7 of key
-// 4kg+j.  Output o[i] holds keys 4kg..4kg+3 of dim 8dc+i.
-__device__ __forceinline__ void transpose4x8(const u32x4 r[4], u32x2 o[8]) {
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int w = i >> 1;
-    uint32_t x01, x23;
-    if ((i & 1) == 0) {
-      x01 = (r[0][w] & 0xffffu) | (r[1][w] << 16);
-      x23 = (r[2][w] & 0xffffu) | (r[3][w] << 16);
-    } else {
-      x01 = (r[0][w] >> 16) | (r[1][w] & 0xffff0000u);
-      x23 = (r[2][w] >> 16) | (r[3][w] & 0xffff0000u);
-    }
-    o[i] = u32x2{x01, x23};
-  }
-}
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+typedef __attribute__((address_space(3))) void lds_void;
 
-__device__ __forceinline__ void lds_store16(char* lds, int off, u32x4 v) {
-  *reinterpret_cast<u32x4*>(lds + off) = v;
-}
-__device__ __forceinline__ void lds_store8(char* lds, int off, u32x2 v) {
-  *reinterpret_cast<u32x2*>(lds + off) = v;
-}
 __device__ __forceinline__ u32x4 lds_load16(const char* lds, int off) {
   return *reinterpret_cast<const u32x4*>(lds + off);
 }
-__device__ __forceinline__ u32x2 lds_load8(const char* lds, int off) {
-  return *reinterpret_cast<const u32x2*>(lds + off);
-}
 __device__ __forceinline__ u32x4 gload16(const uint16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
 
-// A-fragment of K for sub-tile kt, head-dim step ds (lane: key row kt*32+col,
-// dims 16ds + 8*half + 0..7).  lds_k points at the K region.
-template <int BK>
-__device__ __forceinline__ bf16x8 k_frag(const char* lds_k, int kt, int ds, int col, int half) {
-  return as_bf16x8(lds_load16(lds_k, TileLayout<BK>::k_off(kt * 32 + col, 2 * ds + half)));
+// One 16-byte-per-lane direct load: lane i's 16 bytes at src land at
+// lds_dst + 16*i (lds_dst must be the same for the whole wave).
+__device__ __forceinline__ void direct_load16(const uint16_t* src, char* lds_dst) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(src, (lds_void*)(lds_dst), 16, 0, 0);
+#endif
 }
 
-// A-fragment of V^T for output dim tile dt and key step (kt, s): lane holds
-// dim dt*32+col at keys kt*32+16s + {4h..4h+3} then {8+4h..8+4h+3}, h = half;
-// this is the key order of the P^T B-fragment taken from accumulator
-// registers 8s..8s+7 of the score sub-tile kt.  lds_v points at the V^T region.
-template <int BK>
-__device__ __forceinline__ bf16x8 v_frag(const char* lds_v, int dt, int kt, int s, int col, int half) {
-  const int d = dt * 32 + col;
-  const int u = 8 * kt + 4 * s + half;
-  u32x2 a = lds_load8(lds_v, TileLayout<BK>::v_off(d, u));
-  u32x2 b = lds_load8(lds_v, TileLayout<BK>::v_off(d, u + 2));
-  return as_bf16x8(u32x4{a[0], a[1], b[0], b[1]});
+// Issue the direct global->LDS loads of one KV block into `buf`: the calling
+// wave issues loads wave, wave+NW, ... of each region.  Rows past kv_len load
+// the last valid key instead (always masked: score -inf, weight exactly 0).
+template <int BK, int NW>
+__device__ __forceinline__ void issue_block_loads(char* buf, const uint16_t* kb, const uint16_t* vb,
+                                                  int64_t row_stride, int64_t key0, int64_t kv_len) {
+  using L = TileLayout<BK>;
+  static_assert(L::kLoadsPerRegion % NW == 0, "loads must divide over the waves");
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  const int lane = threadIdx.x & 63;
+  const int p = lane & 15;
+#pragma unroll
+  for (int i = 0; i < L::kLoadsPerRegion / NW; ++i) {
+    const int n = wave + NW * i;
+    const int r = 4 * n + (lane >> 4);
+    int64_t key = key0 + r;
+    key = key < kv_len ? key : kv_len - 1;
+    const uint16_t* krow = kb + key * row_stride;
+    const uint16_t* vrow = vb + key * row_stride;
+    direct_load16(krow + ((p ^ L::k_swz(r)) << 3), buf + n * 1024);
+    direct_load16(vrow + ((p ^ L::v_swz(r)) << 3), buf + L::kKBytes + n * 1024);
+  }
 }
+
+// Wait until this wave's direct loads have landed in LDS (vmcnt(0)).
+__device__ __forceinline__ void wait_direct_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// A-fragment of K for sub-tile kt, head-dim step ds (lane: key row kt*32+col,
+// dims 16ds + 8*half + 0..7).
+template <int BK>
+__device__ __forceinline__ bf16x8 k_frag(const char* lds, int kt, int ds, int col, int half) {
+  return as_bf16x8(lds_load16(lds, TileLayout<BK>::k_off(kt * 32 + col, 2 * ds + half)));
+}
+
+// A-fragment of V^T for output dim tile dt and key step (kt, s): lane l holds
+// dim dt*32 + l%32 at keys kb + {4h..4h+3} then kb + {8+4h..8+4h+3},
+// kb = kt*32 + 16s, h = l/32 — the key order of the P^T B-fragment taken from
+// accumulator registers 8s..8s+7 of score sub-tile kt.  Two transposed reads:
+// in each 16-lane group, lane 4k+j reads dims d0+4j..d0+4j+3 of key row
+// base+k and receives dim d0+i of the four rows.
+template <int BK>
+__device__ __forceinline__ bf16x8 v_frag(const char* lds, int dt, int kt, int s) {
+  using L = TileLayout<BK>;
+  const int lane = threadIdx.x & 63;
+  const int i = lane & 15;
+  const int g = lane >> 4;
+  const int h = g >> 1;
+  const int k = i >> 2;
+  const int j = i & 3;
+  const int c = dt * 4 + 2 * (g & 1) + (j >> 1);
+  const int r1 = kt * 32 + 16 * s + 4 * h + k;
+  const int r2 = r1 + 8;
+  const char* p1 = lds + L::v_off(r1, c) + (j & 1) * 8;
+  const char* p2 = lds + L::v_off(r2, c) + (j & 1) * 8;
+  v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p1));
+  v4i16 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p2));
+  typedef short v8i16 __attribute__((ext_vector_type(8)));
+  v8i16 ab = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return __builtin_bit_cast(bf16x8, ab);
+}
+
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 
 }  // namespace rla

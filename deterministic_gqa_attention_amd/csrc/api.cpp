@@ -226,6 +226,8 @@ rla_status rla_attn_decode_paged(const rla_attn_params* p, const void* q, const 
   d.items_lse = items_lse;
   d.num_pages = num_pages;
   d.P = page_size;
+  d.log2_P = 0;
+  while ((1 << d.log2_P) < page_size) ++d.log2_P;  // page_size divides 64 or 128: a power of two
   d.max_pages = max_pages_per_seq;
   d.Bd = batch;
   d.Hq = p->num_q_heads;
@@ -234,6 +236,20 @@ rla_status rla_attn_decode_paged(const rla_attn_params* p, const void* q, const 
   d.max_blocks = static_cast<int32_t>(max_blocks);
   d.len_cap = static_cast<int32_t>(cap);
   d.c = score_scale(p);
+  d.unit_blocks = rla::kDecodeUnitBlocks;
+  if (host_context_lens != nullptr) {
+    // compact grid: exactly the units the lengths need
+    int64_t units = 0;
+    for (int i = 0; i < batch; ++i) {
+      const int64_t nb = (host_context_lens[i] + p->kv_block_size - 1) / p->kv_block_size;
+      units += (nb + rla::kDecodeUnitBlocks - 1) / rla::kDecodeUnitBlocks;
+    }
+    d.compact = 1;
+    d.n_units = units;
+  } else {
+    d.compact = 0;
+    d.n_units = static_cast<int64_t>(batch) * ((max_blocks + rla::kDecodeUnitBlocks - 1) / rla::kDecodeUnitBlocks);
+  }
   const bool f32 = p->out_dtype == RLA_DT_FP32;
   hipStream_t s = static_cast<hipStream_t>(hip_stream);
   hipError_t e = rla::launch_decode_items(d, p->kv_block_size, f32, s);

@@ -1,17 +1,19 @@
-// Paged-KV decode, pass 1 (gfx950): one workgroup per (sequence, kv head,
-// KV block) computes the block's partial state for the q heads of the group
-// and writes it to the caller's workspace; pass 2 (fold.hip) folds the items
-// of each row in ascending block index.
+// Paged-KV decode, pass 1 (gfx950): one workgroup per (kv head, unit of
+// consecutive KV blocks of one sequence) computes each block's partial state
+// for the q heads of the group and writes it to the caller's workspace; pass 2
+// (fold.hip) folds the items of each row in ascending block index.  The cut
+// into units is fixed by the lengths alone and never changes what any item
+// holds.  Decode is bound by reading the KV cache, so the next two blocks are
+// kept in flight in registers (K as MFMA A-fragments, V rows bound for LDS)
+// while the current one is computed, and two workgroups share a CU.
 //
 // Keys are gathered through the page table: key j of sequence s is slot j % P
-// of page page_table[s][j / P] in a pool laid out [page][kv head][slot][dim];
-// the workgroup stages the block in LDS with direct global->LDS loads whose
-// per-lane source addresses do the gather.  The per-(row, block) arithmetic is
-// the same as in the prefill kernel (same LDS layout and fragments, same MFMA
-// shape and operand order, same softmax tree, same PV chain), only split over
-// the four waves: wave w computes score sub-tile w and output dim tile w, and
-// the block max, sub-tile sums and bf16 P go through LDS.  Rows are the
-// group's q heads for the one query token (columns >= G are zero padding).
+// of page page_table[s][j / P] in a pool laid out [page][kv head][slot][dim].
+// The per-(row, block) arithmetic is the same as in the prefill kernel (same
+// fragments, MFMA shape and operand order, softmax tree and PV chain), only
+// split over the four waves: wave w computes score sub-tile w and output dim
+// tile w, and the block max, sub-tile sums and bf16 P go through LDS.  Rows
+// are the group's q heads for the one query token (columns >= G are zero).
 #include "kernels.hpp"
 #include "tile.hpp"
 
@@ -25,87 +27,152 @@ template <int BK, bool F32>
 struct DecodeLds {
   static constexpr int NKT = BK / 32;
   static constexpr int kPBytesPerTile = 64 * 32 * (F32 ? 2 : 1);  // 64 lanes x 16 bf16 (x2 hi/lo)
-  static constexpr int kPOff = TileLayout<BK>::kBytes;
+  static constexpr int kMaxUnitPages = kDecodeUnitBlocks * BK;     // page ids of one unit (page size >= 1)
+  static constexpr int kVOff = 0;                                 // V region only (no K in LDS)
+  static constexpr int kPOff = TileLayout<BK>::kVBytes;
   static constexpr int kMaxOff = kPOff + NKT * kPBytesPerTile;
   static constexpr int kSumOff = kMaxOff + NKT * 32 * 4;
-  static constexpr int kBytes = kSumOff + NKT * 32 * 4;
+  static constexpr int kPageOff = kSumOff + NKT * 32 * 4;
+  static constexpr int kBytes = kPageOff + kMaxUnitPages * 4;
 };
 
-// Element offset of key `key` of sequence `seq`, kv head hk, in the pool.
-// key < len <= len_cap <= max_pages * P keeps the table read in its row; a
-// page id outside [0, num_pages) is never dereferenced (ok = false).
-__device__ __forceinline__ int64_t page_row_off(const DecodeArgs& a, int seq, int hk, int64_t key, bool& ok) {
-  const int32_t page = a.page_table[static_cast<int64_t>(seq) * a.max_pages + key / a.P];
-  ok = page >= 0 && page < a.num_pages;
-  return ((static_cast<int64_t>(ok ? page : 0) * a.Hkv + hk) * a.P + key % a.P) * kHeadDim;
+// The unit's slice of the page table, copied to LDS once so that the per-row
+// page lookups are LDS reads and never wait behind the KV loads in flight
+// (vector loads retire in order).
+struct UnitPages {
+  const int32_t* ids;  // LDS: page ids of pages first .. first+count-1 of the sequence
+  int first;
+};
+
+// Element offset of key `key` (a key of the unit, key < len) of kv head hk in
+// the pool.  Page ids outside [0, num_pages) are clamped into the pool, so a
+// bad table cannot fault (its result is unspecified).
+__device__ __forceinline__ int64_t page_row_off(const DecodeArgs& a, const UnitPages& up, int hk, int key) {
+  int page = up.ids[(key >> a.log2_P) - up.first];
+  page = page < 0 ? 0 : (page >= a.num_pages ? static_cast<int>(a.num_pages - 1) : page);
+  const int64_t row = (static_cast<int64_t>(page * a.Hkv + hk) << a.log2_P) + (key & ((1 << a.log2_P) - 1));
+  return row * kHeadDim;
 }
 
-// Direct global->LDS loads of one KV block gathered through the page table,
-// in the layout of TileLayout (rows past len load key len-1: masked).
+// Registers holding one KV block in flight: the calling wave's K sub-tile as
+// MFMA A-fragments (waves < NKT) and this thread's share of V rows.  Rows past
+// len read key len-1 instead (their scores are masked, their weights are 0).
 template <int BK>
-__device__ __forceinline__ void issue_paged_loads(char* buf, const DecodeArgs& a, int seq, int hk, int64_t key0,
-                                                  int64_t len) {
-  using L = TileLayout<BK>;
-  constexpr int NW = kThreads / 64;
-  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
-  const int lane = threadIdx.x & 63;
-  const int p = lane & 15;
+struct BlockRegs {
+  static constexpr int NKT = BK / 32;
+  static constexpr int VIT = BK * 16 / kThreads;  // 16-byte V chunks per thread
+  u32x4 k[kDSteps];
+  u32x4 v[VIT];
+
+  __device__ __forceinline__ void load(const DecodeArgs& a, const UnitPages& up, int hk, int key0, int len) {
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    if (wave < NKT) {
+      const int key = min(key0 + wave * 32 + (lane & 31), len - 1);
+      const uint16_t* row = a.k_pool + page_row_off(a, up, hk, key) + 8 * (lane >> 5);
 #pragma unroll
-  for (int i = 0; i < L::kLoadsPerRegion / NW; ++i) {
-    const int n = wave + NW * i;
-    const int r = 4 * n + (lane >> 4);
-    int64_t key = key0 + r;
-    key = key < len ? key : len - 1;
-    bool ok;
-    const int64_t off = page_row_off(a, seq, hk, key, ok);  // ok == false: page 0 row (masked or caller error)
-    direct_load16(a.k_pool + off + ((p ^ L::k_swz(r)) << 3), buf + n * 1024);
-    direct_load16(a.v_pool + off + ((p ^ L::v_swz(r)) << 3), buf + L::kKBytes + n * 1024);
+      for (int ds = 0; ds < kDSteps; ++ds) k[ds] = gload16(row + 16 * ds);
+    }
+    const int c = tid & 15;
+    int64_t off[VIT];
+#pragma unroll
+    for (int i = 0; i < VIT; ++i) off[i] = page_row_off(a, up, hk, min(key0 + (tid >> 4) + (kThreads / 16) * i, len - 1));
+#pragma unroll
+    for (int i = 0; i < VIT; ++i) v[i] = gload16(a.v_pool + off[i] + 8 * c);
   }
+
+  // V rows into the (key-major, swizzled) V region of TileLayout.
+  __device__ __forceinline__ void store_v(char* lv) const {
+    using L = TileLayout<BK>;
+    const int tid = threadIdx.x;
+    const int c = tid & 15;
+#pragma unroll
+    for (int i = 0; i < VIT; ++i) {
+      const int r = (tid >> 4) + (kThreads / 16) * i;
+      *reinterpret_cast<u32x4*>(lv + L::v_rel(r, c)) = v[i];
+    }
+  }
+};
+
+__device__ __forceinline__ int64_t clamp_len(const DecodeArgs& a, int seq) {
+  int64_t len = a.ctx_lens[seq];
+  return len < 0 ? 0 : (len > a.len_cap ? a.len_cap : len);
 }
 
+// Map a unit index to (sequence, first block, block count).  Compact grids
+// walk the sequences in order (lane-parallel prefix sum of units per
+// sequence, 64 sequences per step); otherwise unit u is unit u / Bd of
+// sequence u % Bd.  Returns false for an idle unit.
+template <int BK>
+__device__ __forceinline__ bool locate_unit(const DecodeArgs& a, int64_t u, int& seq, int64_t& blk0, int64_t& blk1,
+                                            int64_t& len) {
+  const int U = a.unit_blocks;
+  if (!a.compact) {
+    seq = static_cast<int>(u % a.Bd);
+    len = clamp_len(a, seq);
+    const int64_t nb = (len + BK - 1) / BK;
+    blk0 = (u / a.Bd) * U;
+    blk1 = min(blk0 + U, nb);
+    return blk0 < nb;
+  }
+  const int lane = threadIdx.x & 63;
+  int64_t before = 0;  // units of the sequences already passed
+  for (int s0 = 0; s0 < a.Bd; s0 += 64) {
+    const int s = s0 + lane;
+    int64_t nu = 0;
+    if (s < a.Bd) {
+      const int64_t l = clamp_len(a, s);
+      nu = ((l + BK - 1) / BK + U - 1) / U;
+    }
+    int64_t incl = nu;  // inclusive prefix sum over the 64 lanes
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int64_t y = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += y;
+    }
+    const int64_t total = __shfl(incl, 63, 64);
+    if (u < before + total) {
+      // first lane whose inclusive sum exceeds u - before
+      const unsigned long long m = __ballot(incl > u - before);
+      const int hit = __ffsll(static_cast<long long>(m)) - 1;
+      const int64_t excl = __shfl(incl - nu, hit, 64);
+      seq = s0 + hit;
+      len = clamp_len(a, seq);
+      const int64_t nb = (len + BK - 1) / BK;
+      blk0 = (u - before - excl) * U;
+      blk1 = min(blk0 + U, nb);
+      return blk0 < nb;
+    }
+    before += total;
+  }
+  return false;
+}
+
+// One block's partial states for the group's heads, from the K fragments in
+// registers (waves < NKT) and the V tile in LDS.
 template <int BK, bool F32>
-__global__ __launch_bounds__(kThreads) void decode_items_kernel(const DecodeArgs a) {
+__device__ __forceinline__ void decode_block(const DecodeArgs& a, char* lds, const BlockRegs<BK>& br,
+                                             const bf16x8 (&qf)[kDSteps], int seq, int hk, int64_t blk,
+                                             int64_t len) {
   using Lay = DecodeLds<BK, F32>;
   constexpr int NKT = Lay::NKT;
-  __shared__ __attribute__((aligned(16))) char lds[Lay::kBytes];
+  const char* lv = lds + Lay::kVOff;  // V rows at lv + TileLayout::v_rel(...)
   char* lp = lds + Lay::kPOff;
   float* red_max = reinterpret_cast<float*>(lds + Lay::kMaxOff);
   float* red_sum = reinterpret_cast<float*>(lds + Lay::kSumOff);
-
-  const int64_t x = blockIdx.x;
-  const int hk = static_cast<int>(x % a.Hkv);
-  const int seq = static_cast<int>((x / a.Hkv) % a.Bd);
-  const int64_t blk = x / (static_cast<int64_t>(a.Hkv) * a.Bd);
-  int64_t len = a.ctx_lens[seq];
-  len = len < 0 ? 0 : (len > a.len_cap ? a.len_cap : len);
-  const int64_t nb = (len + BK - 1) / BK;
-  if (blk >= nb) return;  // uniform across the workgroup
-  const int64_t key0 = blk * BK;
-
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
   const int col = lane & 31;
   const int half = lane >> 5;
-
-  issue_paged_loads<BK>(lds, a, seq, hk, key0, len);
-
-  // Q fragments of the group's heads (columns >= G are zero)
-  bf16x8 qf[kDSteps];
-  {
-    const bool qok = col < a.G;
-    const uint16_t* qrow = a.q + (static_cast<int64_t>(seq) * a.Hq + hk * a.G + (qok ? col : 0)) * kHeadDim + 8 * half;
-#pragma unroll
-    for (int ds = 0; ds < kDSteps; ++ds) qf[ds] = as_bf16x8(qok ? gload16(qrow + 16 * ds) : u32x4{0, 0, 0, 0});
-  }
-  wait_direct_loads();
-  __syncthreads();
+  const int64_t key0 = blk * BK;
 
   // ---- scores of sub-tile kt = wave (waves < NKT)
   f32x16 s = f32x16{};
   if (wave < NKT) {
 #pragma unroll
-    for (int ds = 0; ds < kDSteps; ++ds) s = mfma(k_frag<BK>(lds, wave, ds, col, half), qf[ds], s);
+    for (int ds = 0; ds < kDSteps; ++ds) s = mfma(as_bf16x8(br.k[ds]), qf[ds], s);
     float m_lane = kNegInf;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
@@ -117,7 +184,7 @@ __global__ __launch_bounds__(kThreads) void decode_items_kernel(const DecodeArgs
     m_lane = fmaxf(m_lane, partner(m_lane));
     if (half == 0) red_max[wave * 32 + col] = m_lane;
   }
-  __syncthreads();
+  lds_barrier();
 
   float mx = red_max[col];
 #pragma unroll
@@ -151,7 +218,7 @@ __global__ __launch_bounds__(kThreads) void decode_items_kernel(const DecodeArgs
       *reinterpret_cast<u32x4*>(my + 48) = pl[1];
     }
   }
-  __syncthreads();
+  lds_barrier();
 
   float sub[NKT];
 #pragma unroll
@@ -166,7 +233,7 @@ __global__ __launch_bounds__(kThreads) void decode_items_kernel(const DecodeArgs
     const char* pp = lp + kt * Lay::kPBytesPerTile + lane * (F32 ? 64 : 32);
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
-      const bf16x8 vf = v_frag<BK>(lds, dt, kt, st);
+      const bf16x8 vf = v_frag<BK>(lv, dt, kt, st);
       acc = mfma(vf, as_bf16x8(lds_load16(pp, 16 * st)), acc);
       if constexpr (F32) acc = mfma(vf, as_bf16x8(lds_load16(pp, 32 + 16 * st)), acc);
     }
@@ -186,9 +253,71 @@ __global__ __launch_bounds__(kThreads) void decode_items_kernel(const DecodeArgs
   }
 }
 
+// Blocks of the unit are processed in pairs so that the two register sets
+// have static indices: while block b is computed, block b+1 is already in
+// registers and block b+2 is being loaded.
+template <int BK, bool F32>
+__global__ __launch_bounds__(kThreads, 2) void decode_items_kernel(const DecodeArgs a) {
+  using Lay = DecodeLds<BK, F32>;
+  __shared__ __attribute__((aligned(16))) char lds[Lay::kBytes];
+  char* lv = lds + Lay::kVOff;
+
+  const int64_t x = blockIdx.x;
+  const int hk = static_cast<int>(x % a.Hkv);
+  int seq;
+  int64_t blk0, blk1, len;
+  if (!locate_unit<BK>(a, x / a.Hkv, seq, blk0, blk1, len)) return;  // uniform across the workgroup
+
+  const int lane = threadIdx.x & 63;
+  const int col = lane & 31;
+  const int half = lane >> 5;
+
+  // page ids covering the unit's keys [blk0*BK, min(blk1*BK, len))
+  UnitPages up;
+  {
+    int32_t* ids = reinterpret_cast<int32_t*>(lds + Lay::kPageOff);
+    up.ids = ids;
+    up.first = static_cast<int>((blk0 * BK) >> a.log2_P);
+    const int64_t kend = blk1 * BK < len ? blk1 * BK : len;
+    const int64_t count = (kend + a.P - 1) / a.P - up.first;
+    const int32_t* row = a.page_table + static_cast<int64_t>(seq) * a.max_pages + up.first;
+    for (int64_t t = threadIdx.x; t < count; t += kThreads) ids[t] = row[t];
+    __syncthreads();
+  }
+
+  BlockRegs<BK> r0, r1;
+  const int ilen = static_cast<int>(len);
+  r0.load(a, up, hk, static_cast<int>(blk0 * BK), ilen);
+  if (blk0 + 1 < blk1) r1.load(a, up, hk, static_cast<int>((blk0 + 1) * BK), ilen);
+
+  // Q fragments of the group's heads (columns >= G are zero)
+  bf16x8 qf[kDSteps];
+  {
+    const bool qok = col < a.G;
+    const uint16_t* qrow = a.q + (static_cast<int64_t>(seq) * a.Hq + hk * a.G + (qok ? col : 0)) * kHeadDim + 8 * half;
+#pragma unroll
+    for (int ds = 0; ds < kDSteps; ++ds) qf[ds] = as_bf16x8(qok ? gload16(qrow + 16 * ds) : u32x4{0, 0, 0, 0});
+  }
+
+  for (int64_t blk = blk0; blk < blk1; blk += 2) {
+    r0.store_v(lv);
+    lds_barrier();  // V of blk visible
+    decode_block<BK, F32>(a, lds, r0, qf, seq, hk, blk, len);
+    if (blk + 2 < blk1) r0.load(a, up, hk, static_cast<int>((blk + 2) * BK), ilen);
+    lds_barrier();  // everyone done with V / P of blk
+    if (blk + 1 < blk1) {
+      r1.store_v(lv);
+      lds_barrier();
+      decode_block<BK, F32>(a, lds, r1, qf, seq, hk, blk + 1, len);
+      if (blk + 3 < blk1) r1.load(a, up, hk, static_cast<int>((blk + 3) * BK), ilen);
+      lds_barrier();
+    }
+  }
+}
+
 template <int BK, bool F32>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t s) {
-  const int64_t grid = static_cast<int64_t>(a.max_blocks) * a.Bd * a.Hkv;
+  const int64_t grid = a.n_units * a.Hkv;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((decode_items_kernel<BK, F32>), dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, s, a);

@@ -17,6 +17,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
+constexpr int kBatch = 8;  // items in flight per wave
 
 template <bool DECODE, bool F32>
 __global__ __launch_bounds__(kThreads) void fold_kernel(const FoldArgs a) {
@@ -38,18 +39,35 @@ __global__ __launch_bounds__(kThreads) void fold_kernel(const FoldArgs a) {
 
   FoldState st{kNegInf, 0.0f};
   float acc0 = 0.0f, acc1 = 0.0f;
-  for (int i = 0; i < n; ++i) {
-    int64_t idx;  // index of the item's (row, head) record
-    if constexpr (DECODE) {
-      idx = (row * a.n_parts + i) * a.Hq + head;
-    } else {
-      idx = (static_cast<int64_t>(a.order[i]) * a.rows + row) * a.Hq + head;
+  // Items are loaded kBatch at a time (all loads in flight together), then
+  // folded one by one in order.
+  for (int i0 = 0; i0 < n; i0 += kBatch) {
+    float L[kBatch];
+    float2 o[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int i = i0 + j;
+      L[j] = kNegInf;
+      o[j] = float2{0.0f, 0.0f};
+      if (i < n) {
+        int64_t idx;  // index of the item's (row, head) record
+        if constexpr (DECODE) {
+          idx = (row * a.n_parts + i) * a.Hq + head;
+        } else {
+          idx = (static_cast<int64_t>(a.order[i]) * a.rows + row) * a.Hq + head;
+        }
+        L[j] = a.part_lse[idx];
+        o[j] = *reinterpret_cast<const float2*>(a.part_out + idx * kHeadDim + 2 * lane);
+      }
     }
-    const float L = a.part_lse[idx];
-    const float2 o = *reinterpret_cast<const float2*>(a.part_out + idx * kHeadDim + 2 * lane);
-    const FoldStep f = fold_scalars(st, L);
-    acc0 = fold_elem(f, acc0, o.x);
-    acc1 = fold_elem(f, acc1, o.y);
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      if (i0 + j < n) {
+        const FoldStep f = fold_scalars(st, L[j]);
+        acc0 = fold_elem(f, acc0, o[j].x);
+        acc1 = fold_elem(f, acc1, o[j].y);
+      }
+    }
   }
   const Final fin = finalize(st);
   const float o0 = acc0 * fin.r;

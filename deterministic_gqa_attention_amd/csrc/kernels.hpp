@@ -10,6 +10,7 @@ namespace rla {
 
 constexpr int kHeadDimPublic = 128;  // the only head dimension the kernels implement
 constexpr int kMaxParts = 512;  // partial states per merge / owned blocks per emit launch
+constexpr int kDecodeUnitBlocks = 8;  // KV blocks one decode workgroup walks
 
 // Prefill and chunked prefill.  Query row t of batch b sits at absolute
 // position pos0 + t; it attends keys [0, kv_len) (and key <= position when
@@ -38,8 +39,11 @@ struct PrefillArgs {
   uint16_t emit_blocks[kMaxParts];
 };
 
-// Paged decode, pass 1: one workgroup per (sequence, kv head, 128- or 64-key
-// block) writes the block's partial state for the group's q heads.
+// Paged decode, pass 1: one workgroup per (kv head, unit of up to
+// unit_blocks consecutive KV blocks of one sequence) writes each block's
+// partial state for the group's q heads.  compact = 1: the grid enumerates
+// exactly the units the context lengths need (found by a prefix scan of the
+// lengths); compact = 0: the grid is Bd x max_units and idle units exit.
 struct DecodeArgs {
   const uint16_t* q;          // [Bd][Hq][D]
   const uint16_t* k_pool;     // [num_pages][Hkv][P][D]
@@ -50,6 +54,10 @@ struct DecodeArgs {
   float* items_lse;           // [Bd][max_blocks][Hq]
   int64_t num_pages;
   int32_t P, max_pages, Bd, Hq, Hkv, G, max_blocks, len_cap;
+  int32_t log2_P;             // page size is a power of two (it divides the block)
+  int32_t unit_blocks;        // KV blocks per workgroup unit
+  int32_t compact;
+  int64_t n_units;            // units in the grid (per kv head)
   float c;
 };
 

@@ -106,10 +106,11 @@ struct BlockCore {
     f32x16 acc = f32x16{};
     constexpr int NS = NKT * 2;
     bf16x8 vf[2];
-    vf[0] = v_frag<BK>(lds, dt, 0, 0);
+    const char* vbase = lds + TileLayout<BK>::kKBytes;
+    vf[0] = v_frag<BK>(vbase, dt, 0, 0);
 #pragma unroll
     for (int n = 0; n < NS; ++n) {
-      if (n + 1 < NS) vf[(n + 1) & 1] = v_frag<BK>(lds, dt, (n + 1) >> 1, (n + 1) & 1);
+      if (n + 1 < NS) vf[(n + 1) & 1] = v_frag<BK>(vbase, dt, (n + 1) >> 1, (n + 1) & 1);
       const int kt = n >> 1, st = n & 1;
       acc = mfma(vf[n & 1], as_bf16x8(ph[kt][st]), acc);
       if constexpr (F32) acc = mfma(vf[n & 1], as_bf16x8(pl[kt][st]), acc);

@@ -29,7 +29,9 @@ struct TileLayout {
   __device__ static __forceinline__ int v_swz(int r) { return ((r & 3) << 2) ^ ((r >> 2) & 3); }
   // byte offset of logical 16-byte chunk c (dims 8c..8c+7) of key row r
   __device__ static __forceinline__ int k_off(int r, int c) { return r * 256 + ((c ^ k_swz(r)) << 4); }
-  __device__ static __forceinline__ int v_off(int r, int c) { return kKBytes + r * 256 + ((c ^ v_swz(r)) << 4); }
+  // the same within the V region alone, and from the start of the tile
+  __device__ static __forceinline__ int v_rel(int r, int c) { return r * 256 + ((c ^ v_swz(r)) << 4); }
+  __device__ static __forceinline__ int v_off(int r, int c) { return kKBytes + v_rel(r, c); }
 };
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
@@ -88,9 +90,9 @@ __device__ __forceinline__ bf16x8 k_frag(const char* lds, int kt, int ds, int co
 // kb = kt*32 + 16s, h = l/32 — the key order of the P^T B-fragment taken from
 // accumulator registers 8s..8s+7 of score sub-tile kt.  Two transposed reads:
 // in each 16-lane group, lane 4k+j reads dims d0+4j..d0+4j+3 of key row
-// base+k and receives dim d0+i of the four rows.
+// base+k and receives dim d0+i of the four rows.  vbase points at the V region.
 template <int BK>
-__device__ __forceinline__ bf16x8 v_frag(const char* lds, int dt, int kt, int s) {
+__device__ __forceinline__ bf16x8 v_frag(const char* vbase, int dt, int kt, int s) {
   using L = TileLayout<BK>;
   const int lane = threadIdx.x & 63;
   const int i = lane & 15;
@@ -101,8 +103,8 @@ __device__ __forceinline__ bf16x8 v_frag(const char* lds, int dt, int kt, int s)
   const int c = dt * 4 + 2 * (g & 1) + (j >> 1);
   const int r1 = kt * 32 + 16 * s + 4 * h + k;
   const int r2 = r1 + 8;
-  const char* p1 = lds + L::v_off(r1, c) + (j & 1) * 8;
-  const char* p2 = lds + L::v_off(r2, c) + (j & 1) * 8;
+  const char* p1 = vbase + L::v_rel(r1, c) + (j & 1) * 8;
+  const char* p2 = vbase + L::v_rel(r2, c) + (j & 1) * 8;
   v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p1));
   v4i16 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p2));
   typedef short v8i16 __attribute__((ext_vector_type(8)));
@@ -111,5 +113,11 @@ __device__ __forceinline__ bf16x8 v_frag(const char* lds, int dt, int kt, int s)
 }
 
 __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+
+// Workgroup barrier that orders LDS only: waits for this wave's LDS operations
+// (lgkmcnt) and meets the other waves, but leaves global loads in flight, so
+// register prefetches of the next KV block keep streaming across it.  (A full
+// __syncthreads() would also wait for every outstanding global load.)
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 }  // namespace rla

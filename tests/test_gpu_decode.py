@@ -19,7 +19,7 @@ SMALL = gen.DecodeConfig(41, "small paged decode", batch=7, Hq=8, Hkv=2, D=128, 
 SMALL_LENS = np.array([1, 16, 127, 128, 129, 300, 700], np.int32)
 
 
-def _decode(d, cfg, *, block, out_dtype=torch.bfloat16, max_ctx=None, seqs=None):
+def _decode(d, cfg, *, block, out_dtype=torch.bfloat16, max_ctx=None, seqs=None, host_lens=True):
     """Run decode on the inputs in d (numpy); the pools are uploaded once and
     cached in d under "_dev"."""
     if "_dev" not in d:
@@ -30,7 +30,8 @@ def _decode(d, cfg, *, block, out_dtype=torch.bfloat16, max_ctx=None, seqs=None)
     q = d["q"] if seqs is None else d["q"][seqs]
     max_ctx = int(cfg.len_hi) if max_ctx is None else max_ctx
     return api.decode_paged(dev_bf16(q), kp, vp, dev_i32(table), dev_i32(lens), block=block,
-                            max_context_len=max_ctx, host_ctx_lens=lens, out_dtype=out_dtype)
+                            max_context_len=max_ctx, host_ctx_lens=lens if host_lens else None,
+                            out_dtype=out_dtype)
 
 
 @pytest.mark.parametrize("block", [64, 128])
@@ -60,6 +61,18 @@ def test_small_decode_batch_and_relocation():
     ro, rl = _decode(r, SMALL, block=128)
     assert_bitwise(ro, bo, "relocated Out")
     assert_bitwise(rl, bl, "relocated LSE")
+
+
+@pytest.mark.parametrize("block", [64, 128])
+def test_small_decode_without_host_lengths(block):
+    """Without host-side lengths the launch covers every possible unit and idle
+    ones exit; results are bitwise those of the compact launch."""
+    d = gen.decode_inputs(SMALL, lengths=SMALL_LENS)
+    say(f"[decode] no host lengths block={block}")
+    a_o, a_l = _decode(d, SMALL, block=block)
+    b_o, b_l = _decode(d, SMALL, block=block, host_lens=False)
+    assert_bitwise(b_o, a_o, "Out without host lengths")
+    assert_bitwise(b_l, a_l, "LSE without host lengths")
 
 
 def test_decode_equals_prefill_last_row():

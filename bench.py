@@ -21,8 +21,12 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -39,8 +43,45 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA (published)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (published)
 
 
+PROFILES = os.path.join(ROOT, "profiles")
+PREFILL_PROFILE = os.path.join(PROFILES, "prefill_kernel_b4_s4096.md")
+DECODE_PROFILE = os.path.join(PROFILES, "decode_paged_64seq.md")
+TRACE_CMD = {
+    "prefill": "rocprofv3 --kernel-trace --stats -d gpurun_out/prof_prefill -o run --output-format csv -- "
+               "python3 bench.py --only prefill --steps 20 --warmup 3",
+    "decode": "rocprofv3 --kernel-trace --stats -d gpurun_out/prof_decode -o run --output-format csv -- "
+              "python3 bench.py --only decode --decode-steps 10",
+}
+PMC_CMD = ("rocprofv3 --pmc {c} -d gpurun_out/pmc_{c}_{m} -o run --output-format csv -- "
+           "python3 bench.py --only {m} --steps 2 --warmup 1 --decode-steps 2")
+
+
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    """SHA-256 over the HIP sources: counter-derived traffic is used only while
+    the kernels are the ones the counters were taken on."""
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "deterministic_gqa_attention_amd", "csrc", "*"))):
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def profile_traffic(path):
+    """HBM bytes per launch recorded in a profile summary, if it was taken on
+    the current kernel sources; else None."""
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_hash = re.search(r"kernel source sha256: `([0-9a-f]+)`", text)
+    m_bytes = re.search(r"traffic bytes per launch: `([0-9]+)`", text)
+    if not m_hash or not m_bytes or m_hash.group(1) != kernel_source_hash():
+        return None
+    return int(m_bytes.group(1))
 
 
 def cpu_baseline(q, k, v, cfg, seconds):
@@ -79,7 +120,12 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--only", choices=["prefill", "decode", "copy"], default=None,
                     help="run one leg only (for profiler and counter runs)")
+    ap.add_argument("--summarize", metavar="DIR", default=None,
+                    help="write profiles/*.md from the rocprofv3 CSVs under DIR (no GPU work)")
     args = ap.parse_args()
+    if args.summarize:
+        summarize_profiles(args.summarize)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} (WORLD_SIZE={world}) is not supported: "
@@ -174,7 +220,7 @@ def main():
                                "fp32 accumulate", "global_batch": cfg.B, "seq_len": cfg.S, "parallelism": "none",
                    "flop_per_step": flops},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": profile_traffic(PREFILL_PROFILE),
                      "kernel_ms": round(kern_ms, 4)},
         "decode": decode,
         "invariance": {"batch_alone_vs_batch": drift_batch, "cp2_reversed_arrival": drift_cp},
@@ -249,7 +295,7 @@ def decode_leg(args, api, d, dcfg, up, dev, stream):
               "workload": "paged decode, 64 seqs, len U[512,16384] (sum %d), Hq=32 Hkv=8 D=128, page 16, "
                           "1M-slot pool, 128-key blocks, bf16 out" % int(host_lens.sum()),
               "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                           "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None}}
+                           "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": profile_traffic(DECODE_PROFILE)}}
     log(f"decode {dms:.3f} ms, {gbs:.0f} GB/s KV")
     return decode
 
@@ -274,6 +320,138 @@ def copy_calibration(args):
     ms = e0.elapsed_time(e1) / max(1, args.steps)
     print(json.dumps({"only": "copy", "bytes_read": n, "bytes_written": n, "ms": ms,
                       "GBps": 2 * n / (ms * 1e-3) / 1e9}))
+
+
+def _read_csv(path):
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def _pmc_mean(d, counter, mode, name_part):
+    """Mean counter value (KiB per dispatch) of the kernels whose name contains name_part."""
+    path = os.path.join(d, f"pmc_{counter}_{mode}", "run_counter_collection.csv")
+    vals = [float(r["Counter_Value"]) for r in _read_csv(path) if name_part in r["Kernel_Name"]]
+    return sum(vals) / len(vals), len(vals)
+
+
+def summarize_profiles(d):
+    """Turn the kernel-trace stats and the FETCH_SIZE / WRITE_SIZE counter runs
+    under d into profiles/prefill_kernel_b4_s4096.md and profiles/decode_paged_64seq.md.
+    Counter KiB are scaled by what the same counter reads for a plain 1 GiB
+    device copy (the runtime's copy kernel): bytes = KiB * 1024 * factor."""
+    copy_f, _ = _pmc_mean(d, "FETCH_SIZE", "copy", "copyBuffer")
+    copy_w, _ = _pmc_mean(d, "WRITE_SIZE", "copy", "copyBuffer")
+    f_fetch = (1 << 30) / (copy_f * 1024.0)
+    f_write = (1 << 30) / (copy_w * 1024.0)
+    src = kernel_source_hash()
+    cfg, dcfg = gen.CFG2, gen.CFG4
+    lens = gen.decode_lengths(dcfg)
+    kv = gen.decode_kv_bytes(lens, dcfg.Hkv, dcfg.D)
+    pages = int((-(-lens.astype(np.int64) // dcfg.page_size)).sum())
+    dec_alg = kv + dcfg.batch * dcfg.Hq * dcfg.D * 2 * 2 + dcfg.batch * dcfg.Hq * 4 + pages * 4 + dcfg.batch * 4
+    pre_alg = (cfg.B * cfg.S * (cfg.Hq + 2 * cfg.Hkv) * cfg.D * 2 + cfg.B * cfg.S * cfg.Hq * cfg.D * 2
+               + cfg.B * cfg.S * cfg.Hq * 4)
+
+    def stats_rows(mode, parts):
+        rows = _read_csv(os.path.join(d, f"prof_{mode}", "run_kernel_stats.csv"))
+        out = []
+        for r in rows:
+            if any(p in r["Name"] for p in parts):
+                out.append((r["Name"], int(r["Calls"]), float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+                            float(r["MaxNs"]) / 1e3))
+        return out
+
+    def counters(mode, part):
+        fk, n1 = _pmc_mean(d, "FETCH_SIZE", mode, part)
+        wk, n2 = _pmc_mean(d, "WRITE_SIZE", mode, part)
+        return fk, wk, int(round(fk * 1024 * f_fetch)), int(round(wk * 1024 * f_write)), min(n1, n2)
+
+    header = ("Counter scaling: a plain 1 GiB device copy (`python3 bench.py --only copy`) reads "
+              f"FETCH_SIZE = {copy_f:.1f} KiB and WRITE_SIZE = {copy_w:.1f} KiB per dispatch, so "
+              f"fetch bytes = KiB x 1024 x {f_fetch:.4f} and write bytes = KiB x 1024 x {f_write:.4f}.\n")
+    cmds = "\n".join("    " + PMC_CMD.format(c=c, m=m) for c in ("FETCH_SIZE", "WRITE_SIZE")
+                     for m in ("prefill", "decode", "copy"))
+
+    # prefill
+    st = stats_rows("prefill", ["prefill_kernel"])
+    fk, wk, fb, wb, n = counters("prefill", "prefill_kernel")
+    name, calls, avg, mn, mx = st[0]
+    flops = cfg.flops()
+    lines = [
+        "# Prefill kernel, causal B=4 S=4096 Hq=32 Hkv=8 D=128, 128-key blocks, bf16 out",
+        "",
+        "Kernel trace (all dispatches are the timed workload):",
+        "",
+        "    " + TRACE_CMD["prefill"],
+        "",
+        "| kernel | calls | avg us | min us | max us | TFLOP/s at avg | frac of 2500 |",
+        "|---|---|---|---|---|---|---|",
+        f"| `{name}` | {calls} | {avg:.1f} | {mn:.1f} | {mx:.1f} | {flops / (avg * 1e-6) / 1e12:.1f} | "
+        f"{flops / (avg * 1e-6) / 1e12 / PEAK_BF16_TFLOPS:.4f} |",
+        "",
+        f"Algorithmic work per launch: {flops:.6e} flop (4·D·Hq·B·S(S+1)/2); algorithmic HBM bytes "
+        f"{pre_alg} (Q, K, V in; Out bf16, LSE out).",
+        "",
+        "HBM counters, one run per counter:",
+        "",
+        cmds,
+        "",
+        header,
+        f"| counter | KiB per dispatch (mean of {n}) | bytes |",
+        "|---|---|---|",
+        f"| FETCH_SIZE | {fk:.1f} | {fb} |",
+        f"| WRITE_SIZE | {wk:.1f} | {wb} |",
+        "",
+        f"traffic bytes per launch: `{fb + wb}` ({(fb + wb) / pre_alg:.2f} x algorithmic)",
+        "",
+        f"kernel source sha256: `{src}`",
+        "",
+    ]
+    with open(PREFILL_PROFILE, "w") as f:
+        f.write("\n".join(lines))
+
+    # decode
+    st = stats_rows("decode", ["decode_items_kernel", "fold_kernel"])
+    ci = counters("decode", "decode_items_kernel")
+    cf = counters("decode", "fold_kernel")
+    total_us = sum(r[2] for r in st)
+    lines = [
+        "# Paged decode, 64 sequences, lengths U[512,16384], page 16, 128-key blocks, bf16 out",
+        "",
+        f"Drawn lengths sum to {int(lens.sum())} tokens; K+V bytes read {kv}; algorithmic bytes per decode call "
+        f"{dec_alg} (KV, Q, Out, LSE, used page-table entries, lengths).",
+        "",
+        "Kernel trace (decode = items kernel + fold kernel; caches flushed by a 1 GiB fill between calls):",
+        "",
+        "    " + TRACE_CMD["decode"],
+        "",
+        "| kernel | calls | avg us | min us | max us |",
+        "|---|---|---|---|---|",
+    ] + [f"| `{r[0]}` | {r[1]} | {r[2]:.1f} | {r[3]:.1f} | {r[4]:.1f} |" for r in st] + [
+        "",
+        f"Sum of averages {total_us:.1f} us -> {dec_alg / (total_us * 1e-6) / 1e9:.1f} GB/s algorithmic "
+        f"({dec_alg / (total_us * 1e-6) / 1e9 / PEAK_HBM_GBS:.4f} of 8000 GB/s).",
+        "",
+        "HBM counters, one run per counter:",
+        "",
+        cmds,
+        "",
+        header,
+        "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | fetch bytes | write bytes |",
+        "|---|---|---|---|---|",
+        f"| decode_items_kernel | {ci[0]:.1f} | {ci[1]:.1f} | {ci[2]} | {ci[3]} |",
+        f"| fold_kernel | {cf[0]:.1f} | {cf[1]:.1f} | {cf[2]} | {cf[3]} |",
+        "",
+        f"traffic bytes per launch: `{ci[2] + ci[3] + cf[2] + cf[3]}` (both kernels; "
+        f"{(ci[2] + ci[3] + cf[2] + cf[3]) / dec_alg:.3f} x algorithmic; the per-block partial states "
+        "written by the items kernel and read back by the fold are the excess)",
+        "",
+        f"kernel source sha256: `{src}`",
+        "",
+    ]
+    with open(DECODE_PROFILE, "w") as f:
+        f.write("\n".join(lines))
+    print(f"wrote {PREFILL_PROFILE} and {DECODE_PROFILE}")
 
 
 if __name__ == "__main__":

@@ -24,11 +24,15 @@
 //           (FP32-output mode: P = hi + lo, two MFMAs per key step)
 //   O_b   = acc_b * (1 / l_b);   L_b = (m_t + log2 l_b) * ln 2
 //   empty row (no unmasked key) -> (O_b, L_b) = (0, -inf)
-// Fold over blocks in ascending index from the empty state (m, l, acc):
+// Fold over blocks in ascending index from the empty state (m, l, acc), with
+// a lazily moved reference m (tau = 8, natural-log units):
 //   first non-empty item: (m, l, acc) := (L_b, 1, O_b)
-//   later items: m' = max(m, L_b), alpha = m == m' ? 1 : e^(m - m'),
-//                beta = L_b == m' ? 1 : e^(L_b - m'),
-//                l = l*alpha + beta, acc = fma(O_b, beta, acc*alpha)
+//   L_b <= m + tau ("add"):   beta = e^(L_b - m), l = l + beta,
+//                             acc = fma(O_b, beta, acc)
+//   L_b >  m + tau ("move"):  alpha = e^(m - L_b), m = L_b,
+//                             l = l*alpha + 1, acc = fma(O_b, 1, acc*alpha)
+//   (weights stay below e^tau, so nothing overflows; the reference moves only
+//   on large jumps, so almost every step costs one fma per element)
 // Finalize: O = acc * (1 / l), LSE = m + log2(l) * ln 2 (natural log);
 //           no item at all -> (0, -inf).
 // The library is compiled with -ffp-contract=off, so no multiply-add is fused
@@ -140,12 +144,16 @@ struct FoldState {
   float l;  // running sum of exp(L_i - m)
 };
 
-enum FoldMode : int { kFoldSkip = 0, kFoldFirst = 1, kFoldCombine = 2 };
+// Distance (natural log) the block LSE must exceed the reference by before
+// the reference moves.
+constexpr float kFoldTau = 8.0f;
+
+enum FoldMode : int { kFoldSkip = 0, kFoldFirst = 1, kFoldAdd = 2, kFoldMove = 3 };
 
 struct FoldStep {
   int mode;
-  float alpha;
-  float beta;
+  float alpha;  // kFoldMove: e^(m_old - L); else 1
+  float beta;   // kFoldAdd: e^(L - m); kFoldMove: 1
 };
 
 // Scalar part of one fold step (updates m and l).
@@ -159,26 +167,30 @@ __device__ __forceinline__ FoldStep fold_scalars(FoldState& st, float L) {
     f.mode = kFoldFirst;
     st.m = L;
     st.l = 1.0f;
+  } else if (L > st.m + kFoldTau) {
+    f.mode = kFoldMove;
+    f.alpha = fold_exp(st.m - L);
+    const float la = st.l * f.alpha;
+    st.l = la + 1.0f;
+    st.m = L;
   } else {
-    f.mode = kFoldCombine;
-    float mn = fmaxf(st.m, L);
-    f.alpha = (st.m == mn) ? 1.0f : fold_exp(st.m - mn);
-    f.beta = (L == mn) ? 1.0f : fold_exp(L - mn);
-    float la = st.l * f.alpha;
-    st.l = la + f.beta;
-    st.m = mn;
+    f.mode = kFoldAdd;
+    f.beta = fold_exp(L - st.m);
+    st.l = st.l + f.beta;
   }
   return f;
 }
 
 // Element part of one fold step.
-__device__ __forceinline__ float fold_combine(float acc, float o, float alpha, float beta) {
-  float sa = acc * alpha;
-  return fmaf(o, beta, sa);
+__device__ __forceinline__ float fold_add(float acc, float o, float beta) { return fmaf(o, beta, acc); }
+__device__ __forceinline__ float fold_move(float acc, float o, float alpha) {
+  const float sa = acc * alpha;
+  return fmaf(o, 1.0f, sa);
 }
 __device__ __forceinline__ float fold_elem(const FoldStep& f, float acc, float o) {
-  float c = fold_combine(acc, o, f.alpha, f.beta);
-  return f.mode == kFoldCombine ? c : (f.mode == kFoldFirst ? o : acc);
+  const float a = fold_add(acc, o, f.beta);
+  const float m = fold_move(acc, o, f.alpha);
+  return f.mode == kFoldAdd ? a : (f.mode == kFoldMove ? m : (f.mode == kFoldFirst ? o : acc));
 }
 
 // Finalize scalars: O = acc * r, LSE natural log.

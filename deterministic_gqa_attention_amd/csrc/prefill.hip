@@ -39,8 +39,9 @@ struct BlockCore {
   float l_b;         // block sum of p
 
   // S^T, mask, max, p = 2^fma(s, c, -m), canonical sum, bf16 P.
-  __device__ __forceinline__ void softmax(const char* lds, const bf16x8 (&qf)[kDSteps], int64_t key0,
-                                          int64_t kv_len, int causal, int64_t qpos, bool need_mask, float c) {
+  // Positions are 32-bit (sequence lengths stay below 2^31).
+  __device__ __forceinline__ void softmax(const char* lds, const bf16x8 (&qf)[kDSteps], int key0, int kv_len,
+                                          int causal, int qpos, bool need_mask, float c) {
     const int lane = threadIdx.x & 63;
     const int col = lane & 31;
     const int half = lane >> 5;
@@ -61,18 +62,23 @@ struct BlockCore {
       sched_fence();
     }
     float mx = kNegInf;
+    if (need_mask) {  // wave-uniform: only blocks on the causal diagonal or past kv_len
+      const int kbase = key0 + 4 * half;
 #pragma unroll
-    for (int kt = 0; kt < NKT; ++kt) {
+      for (int kt = 0; kt < NKT; ++kt) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        float d = s[kt][v];
-        if (need_mask) {
-          const int64_t key = key0 + kt * 32 + acc_row(v, half);
+        for (int v = 0; v < 16; ++v) {
+          const int key = kbase + kt * 32 + 8 * (v >> 2) + (v & 3);
           const bool ok = key < kv_len && (!causal || key <= qpos);
-          d = ok ? d : kNegInf;
-          s[kt][v] = d;
+          s[kt][v] = ok ? s[kt][v] : kNegInf;
+          mx = fmaxf(mx, s[kt][v]);
         }
-        mx = fmaxf(mx, d);
+      }
+    } else {
+#pragma unroll
+      for (int kt = 0; kt < NKT; ++kt) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kt][v]);
       }
     }
     mx = fmaxf(mx, partner(mx));
@@ -128,7 +134,8 @@ struct TileMap {
 
 __device__ __forceinline__ TileMap map_tile(const PrefillArgs& a, int64_t wg) {
   TileMap m;
-  const int wave = threadIdx.x >> 6;
+  // wave index made provably uniform, so per-wave decisions are scalar branches
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int col = threadIdx.x & 31;
   const int n_bh = a.B * a.Hkv * a.hsubs;
   const int bh = static_cast<int>(wg % n_bh);
@@ -149,16 +156,14 @@ __device__ __forceinline__ TileMap map_tile(const PrefillArgs& a, int64_t wg) {
   return m;
 }
 
-// One fold step of output dim tile dt (acc_b -> O_b -> running acc).
+// One fold step of output dim tile dt (acc_b -> O_b -> running acc).  When
+// every lane of the wave takes the "add" step (the common case) the select
+// of fold_elem is skipped; the arithmetic is the same.
 __device__ __forceinline__ void fold_tile(f32x16& acc, const f32x16& ab, const ItemScalars& sc, const FoldStep& f,
-                                          bool all_fast, bool all_comb) {
-  if (all_fast) {
-    // acc * 1 == acc exactly: the same bits as the general combine below.
+                                          bool all_add) {
+  if (all_add) {
 #pragma unroll
-    for (int v = 0; v < 16; ++v) acc[v] = fmaf(item_out(ab[v], sc), f.beta, acc[v]);
-  } else if (all_comb) {
-#pragma unroll
-    for (int v = 0; v < 16; ++v) acc[v] = fold_combine(acc[v], item_out(ab[v], sc), f.alpha, f.beta);
+    for (int v = 0; v < 16; ++v) acc[v] = fold_add(acc[v], item_out(ab[v], sc), f.beta);
   } else {
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[v] = fold_elem(f, acc[v], item_out(ab[v], sc));
@@ -211,10 +216,14 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a) 
     const bool active = tile_sees && wave_sees(blk);
     BlockCore<BK, F32> bc;
     if (tile_sees) {
-      issue_block_loads<BK, kWaves>(lds, kb, vb, row_stride, blk * BK, a.kv_len);
+      BlockLoader<BK, kWaves> ld;
+      ld.init(static_cast<int>(row_stride));
+      ld.issue(lds, kb, vb, row_stride, blk * BK, a.kv_len);
       wait_direct_loads();
       __syncthreads();
-      if (active) bc.softmax(lds, qf, blk * BK, a.kv_len, a.causal, tm.qpos, !wave_full(blk), a.c);
+      if (active)
+        bc.softmax(lds, qf, static_cast<int>(blk * BK), static_cast<int>(a.kv_len), a.causal,
+                   static_cast<int>(tm.qpos), !wave_full(blk), a.c);
     }
     const ItemScalars sc = active ? item_scalars(bc.m_t, bc.l_b) : ItemScalars{0.0f, kNegInf};
     const int64_t prow = static_cast<int64_t>(pidx) * a.B * a.Sq + out_row;
@@ -241,32 +250,31 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a) 
 #pragma unroll
     for (int dt = 0; dt < kDTiles; ++dt) acc[dt] = f32x16{};
 
-    if (last_blk >= 0) issue_block_loads<BK, kWaves>(lds, kb, vb, row_stride, 0, a.kv_len);
+    BlockLoader<BK, kWaves> ld;
+    ld.init(static_cast<int>(row_stride));
+    if (last_blk >= 0) ld.issue(lds, kb, vb, row_stride, 0, a.kv_len);
     wait_direct_loads();
     __syncthreads();
 
     for (int64_t blk = 0; blk <= last_blk; ++blk) {
       const char* cur = lds + (blk & 1) * L::kBytes;
       if (blk + 1 <= last_blk)
-        issue_block_loads<BK, kWaves>(lds + ((blk + 1) & 1) * L::kBytes, kb, vb, row_stride, (blk + 1) * BK,
-                                      a.kv_len);
+        ld.issue(lds + ((blk + 1) & 1) * L::kBytes, kb, vb, row_stride, (blk + 1) * BK, a.kv_len);
       if (wave_sees(blk)) {
         BlockCore<BK, F32> bc;
-        bc.softmax(cur, qf, blk * BK, a.kv_len, a.causal, tm.qpos, !wave_full(blk), a.c);
+        bc.softmax(cur, qf, static_cast<int>(blk * BK), static_cast<int>(a.kv_len), a.causal,
+                   static_cast<int>(tm.qpos), !wave_full(blk), a.c);
         const ItemScalars sc = item_scalars(bc.m_t, bc.l_b);
         const FoldStep f = fold_scalars(fs, sc.L);
-        const bool all_fast = __all(f.mode == kFoldCombine && f.alpha == 1.0f);
-        const bool all_comb = __all(f.mode == kFoldCombine);
-        // PV of tile dt is issued before the fold of tile dt-1 so the fold's
-        // VALU work runs while the matrix core computes.
-        f32x16 ab_prev = bc.pv(cur, 0);
-#pragma unroll
-        for (int dt = 1; dt < kDTiles; ++dt) {
-          const f32x16 ab = bc.pv(cur, dt);
-          fold_tile(acc[dt - 1], ab_prev, sc, f, all_fast, all_comb);
-          ab_prev = ab;
-        }
-        fold_tile(acc[kDTiles - 1], ab_prev, sc, f, all_fast, all_comb);
+        const bool all_add = __all(f.mode == kFoldAdd);
+        f32x16 ab0 = bc.pv(cur, 0);
+        f32x16 ab1 = bc.pv(cur, 1);
+        fold_tile(acc[0], ab0, sc, f, all_add);
+        ab0 = bc.pv(cur, 2);
+        fold_tile(acc[1], ab1, sc, f, all_add);
+        ab1 = bc.pv(cur, 3);
+        fold_tile(acc[2], ab0, sc, f, all_add);
+        fold_tile(acc[3], ab1, sc, f, all_add);
       }
       wait_direct_loads();
       __syncthreads();

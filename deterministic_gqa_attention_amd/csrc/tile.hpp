@@ -51,29 +51,59 @@ __device__ __forceinline__ void direct_load16(const uint16_t* src, char* lds_dst
 #endif
 }
 
-// Issue the direct global->LDS loads of one KV block into `buf`: the calling
-// wave issues loads wave, wave+NW, ... of each region.  Rows past kv_len load
-// the last valid key instead (always masked: score -inf, weight exactly 0).
+// Direct global->LDS loads of KV blocks into a tile buffer: the calling wave
+// issues loads wave, wave+NW, ... of each region (1 KiB = 4 key rows each).
+// The lane's element offsets within a block are fixed, so they are computed
+// once; a block that reaches past kv_len takes the clamped path, where rows
+// past kv_len load the last valid key instead (always masked: score -inf,
+// weight exactly 0).
 template <int BK, int NW>
-__device__ __forceinline__ void issue_block_loads(char* buf, const uint16_t* kb, const uint16_t* vb,
-                                                  int64_t row_stride, int64_t key0, int64_t kv_len) {
+struct BlockLoader {
   using L = TileLayout<BK>;
+  static constexpr int NI = L::kLoadsPerRegion / NW;
   static_assert(L::kLoadsPerRegion % NW == 0, "loads must divide over the waves");
-  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
-  const int lane = threadIdx.x & 63;
-  const int p = lane & 15;
-#pragma unroll
-  for (int i = 0; i < L::kLoadsPerRegion / NW; ++i) {
-    const int n = wave + NW * i;
-    const int r = 4 * n + (lane >> 4);
-    int64_t key = key0 + r;
-    key = key < kv_len ? key : kv_len - 1;
-    const uint16_t* krow = kb + key * row_stride;
-    const uint16_t* vrow = vb + key * row_stride;
-    direct_load16(krow + ((p ^ L::k_swz(r)) << 3), buf + n * 1024);
-    direct_load16(vrow + ((p ^ L::v_swz(r)) << 3), buf + L::kKBytes + n * 1024);
+  // Row of load i is r_i = 4*(wave + NW*i) + lane/16; both swizzles depend on
+  // r_i only through bits that do not change with i (NW is a multiple of 4),
+  // so offset i is offset 0 plus the uniform stride i * 4*NW rows.
+  static_assert(NW % 4 == 0, "swizzle bits must not depend on the load index");
+  int koff0;
+  int voff0;
+  int wave;
+
+  __device__ __forceinline__ void init(int row_stride) {
+    wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+    const int lane = threadIdx.x & 63;
+    const int p = lane & 15;
+    const int r = 4 * wave + (lane >> 4);
+    koff0 = r * row_stride + ((p ^ L::k_swz(r)) << 3);
+    voff0 = r * row_stride + ((p ^ L::v_swz(r)) << 3);
   }
-}
+
+  __device__ __forceinline__ void issue(char* buf, const uint16_t* kb, const uint16_t* vb, int64_t row_stride,
+                                        int64_t key0, int64_t kv_len) const {
+    if (key0 + BK <= kv_len) {
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int n = wave + NW * i;
+        const int64_t rows = key0 + 4 * NW * i;  // uniform
+        direct_load16(kb + rows * row_stride + koff0, buf + n * 1024);
+        direct_load16(vb + rows * row_stride + voff0, buf + L::kKBytes + n * 1024);
+      }
+    } else {
+      const int lane = threadIdx.x & 63;
+      const int p = lane & 15;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int n = wave + NW * i;
+        const int r = 4 * n + (lane >> 4);
+        int64_t key = key0 + r;
+        key = key < kv_len ? key : kv_len - 1;
+        direct_load16(kb + key * row_stride + ((p ^ L::k_swz(r)) << 3), buf + n * 1024);
+        direct_load16(vb + key * row_stride + ((p ^ L::v_swz(r)) << 3), buf + L::kKBytes + n * 1024);
+      }
+    }
+  }
+};
 
 // Wait until this wave's direct loads have landed in LDS (vmcnt(0)).
 __device__ __forceinline__ void wait_direct_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
@@ -108,7 +138,7 @@ __device__ __forceinline__ bf16x8 v_frag(const char* vbase, int dt, int kt, int 
   v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p1));
   v4i16 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p2));
   typedef short v8i16 __attribute__((ext_vector_type(8)));
-  v8i16 ab = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  v8i16 ab = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
   return __builtin_bit_cast(bf16x8, ab);
 }
 

@@ -24,15 +24,17 @@
 //           (FP32-output mode: P = hi + lo, two MFMAs per key step)
 //   O_b   = acc_b * (1 / l_b);   L_b = (m_t + log2 l_b) * ln 2
 //   empty row (no unmasked key) -> (O_b, L_b) = (0, -inf)
-// Fold over blocks in ascending index from the empty state (m, l, acc), with
-// a lazily moved reference m (tau = 8, natural-log units):
-//   first non-empty item: (m, l, acc) := (L_b, 1, O_b)
-//   L_b <= m + tau ("add"):   beta = e^(L_b - m), l = l + beta,
-//                             acc = fma(O_b, beta, acc)
-//   L_b >  m + tau ("move"):  alpha = e^(m - L_b), m = L_b,
-//                             l = l*alpha + 1, acc = fma(O_b, 1, acc*alpha)
-//   (weights stay below e^tau, so nothing overflows; the reference moves only
-//   on large jumps, so almost every step costs one fma per element)
+// Fold over blocks in ascending index from the empty state (m, l, acc) =
+// (-inf, 0, 0), with a lazily moved reference m (tau = 8, natural-log units).
+// Every step is acc = fma(O_b, beta, acc * alpha) with:
+//   empty item (L_b = -inf):  alpha = 1, beta = 0          (state unchanged)
+//   first non-empty item:     alpha = 1, beta = 1, m = L_b, l = 1
+//   L_b <= m + tau ("add"):   alpha = 1, beta = e^(L_b - m), l = l + beta
+//   L_b >  m + tau ("move"):  alpha = e^(m - L_b), beta = 1,
+//                             l = l*alpha + 1, m = L_b
+//   (acc * 1 is exact, so a kernel may skip that multiply when no lane of the
+//   wave moves; weights stay below e^tau, so nothing overflows, and the
+//   reference moves only on large jumps, so almost every step is one fma)
 // Finalize: O = acc * (1 / l), LSE = m + log2(l) * ln 2 (natural log);
 //           no item at all -> (0, -inf).
 // The library is compiled with -ffp-contract=off, so no multiply-add is fused
@@ -93,8 +95,30 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
 __device__ __forceinline__ float bf16_lo_to_f32(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf16_hi_to_f32(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
 
-// Exchange with the lane 32 apart (same accumulator column, other row half).
-__device__ __forceinline__ float partner(float x) { return __shfl_xor(x, 32, 64); }
+// Combine a value with the one held by the lane 32 apart (same accumulator
+// column, other row half) without going through LDS: v_permlane32_swap swaps
+// the upper half of one register with the lower half of another, so with two
+// copies of x every lane ends up holding {x[l mod 32], x[l mod 32 + 32]}.
+// max and + are commutative, so both halves get the same bits.  (Inline asm:
+// the compiler builtin for this instruction returns only one of its two
+// results.  The leading s_nop covers a VALU write of the operands just before.)
+__device__ __forceinline__ void lane_pair(float x, float& lo, float& hi) {
+  uint32_t a = __builtin_bit_cast(uint32_t, x);
+  uint32_t b = a;
+  asm("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+  lo = __builtin_bit_cast(float, a);
+  hi = __builtin_bit_cast(float, b);
+}
+__device__ __forceinline__ float pair_max(float x) {
+  float a, b;
+  lane_pair(x, a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  float a, b;
+  lane_pair(x, a, b);
+  return a + b;
+}
 
 // Canonical sum of the 16 values one lane holds for one 32-key sub-tile:
 // a fixed pairwise tree in register order.
@@ -148,12 +172,10 @@ struct FoldState {
 // the reference moves.
 constexpr float kFoldTau = 8.0f;
 
-enum FoldMode : int { kFoldSkip = 0, kFoldFirst = 1, kFoldAdd = 2, kFoldMove = 3 };
-
 struct FoldStep {
-  int mode;
-  float alpha;  // kFoldMove: e^(m_old - L); else 1
-  float beta;   // kFoldAdd: e^(L - m); kFoldMove: 1
+  float alpha;  // "move": e^(m_old - L); else 1
+  float beta;   // "add": e^(L - m); "move", first item: 1; empty item: 0
+  bool move;
 };
 
 // Scalar part of one fold step (updates m and l).
@@ -161,20 +183,19 @@ __device__ __forceinline__ FoldStep fold_scalars(FoldState& st, float L) {
   FoldStep f;
   f.alpha = 1.0f;
   f.beta = 1.0f;
+  f.move = false;
   if (L == kNegInf) {
-    f.mode = kFoldSkip;
+    f.beta = 0.0f;
   } else if (st.m == kNegInf) {
-    f.mode = kFoldFirst;
     st.m = L;
     st.l = 1.0f;
   } else if (L > st.m + kFoldTau) {
-    f.mode = kFoldMove;
+    f.move = true;
     f.alpha = fold_exp(st.m - L);
     const float la = st.l * f.alpha;
     st.l = la + 1.0f;
     st.m = L;
   } else {
-    f.mode = kFoldAdd;
     f.beta = fold_exp(L - st.m);
     st.l = st.l + f.beta;
   }
@@ -182,15 +203,12 @@ __device__ __forceinline__ FoldStep fold_scalars(FoldState& st, float L) {
 }
 
 // Element part of one fold step.
-__device__ __forceinline__ float fold_add(float acc, float o, float beta) { return fmaf(o, beta, acc); }
-__device__ __forceinline__ float fold_move(float acc, float o, float alpha) {
-  const float sa = acc * alpha;
-  return fmaf(o, 1.0f, sa);
-}
 __device__ __forceinline__ float fold_elem(const FoldStep& f, float acc, float o) {
-  const float a = fold_add(acc, o, f.beta);
-  const float m = fold_move(acc, o, f.alpha);
-  return f.mode == kFoldAdd ? a : (f.mode == kFoldMove ? m : (f.mode == kFoldFirst ? o : acc));
+  return fmaf(o, f.beta, acc * f.alpha);
+}
+// The same when alpha == 1 (no lane of the wave moves): acc * 1 is exact.
+__device__ __forceinline__ float fold_elem_nomove(const FoldStep& f, float acc, float o) {
+  return fmaf(o, f.beta, acc);
 }
 
 // Finalize scalars: O = acc * r, LSE natural log.

@@ -181,7 +181,7 @@ __device__ __forceinline__ void decode_block(const DecodeArgs& a, char* lds, con
       s[v] = d;
       m_lane = fmaxf(m_lane, d);
     }
-    m_lane = fmaxf(m_lane, partner(m_lane));
+    m_lane = pair_max(m_lane);
     if (half == 0) red_max[wave * 32 + col] = m_lane;
   }
   lds_barrier();
@@ -196,7 +196,7 @@ __device__ __forceinline__ void decode_block(const DecodeArgs& a, char* lds, con
 #pragma unroll
     for (int v = 0; v < 16; ++v) s[v] = block_p(s[v], a.c, m_use);
     const float aa = tree16(s);
-    const float sum = aa + partner(aa);
+    const float sum = pair_sum(aa);
     if (half == 0) red_sum[wave * 32 + col] = sum;
     u32x4 ph[2], pl[2];
 #pragma unroll

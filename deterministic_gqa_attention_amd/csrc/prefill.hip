@@ -1,24 +1,31 @@
-// Prefill / chunked-prefill kernel for gfx950: fused mode (fold every KV block
-// of the row in ascending global block index and write Out/LSE) and emit mode
-// (write the per-block partial states of a set of owned blocks, which is how a
-// context-parallel shard is emulated on one GPU).
+// Prefill / chunked-prefill kernels for gfx950: fused mode (fold every KV
+// block of the row in ascending global block index and write Out/LSE) and
+// emit mode (write the per-block partial states of a set of owned blocks,
+// which is how a context-parallel shard is emulated on one GPU).
 //
 // Work decomposition: a workgroup of 8 waves (two per SIMD) takes one kv head
 // hk of one batch row and a tile of query positions; each wave owns 32
 // consecutive positions of one q head of the group (an MFMA column tile).
 // Each KV block is staged in LDS once per workgroup by direct global->LDS
-// loads and read by all waves.  In fused mode the LDS is double-buffered: the
-// loads of block b+1 are issued before block b is computed, and one barrier
-// per block hands the buffers over.
-// Per wave and block: S^T = K Q^T (bf16 MFMA 32x32x16, fp32 accumulate), the
-// block softmax on the score registers, and per 32-dim output tile
-// acc_b = V^T P^T (bf16 MFMA), the block item O_b = acc_b / l_b and, in fused
-// mode, its fold into the running state — all with the operations of
-// core.hpp.  Fragment loads are software-pipelined one step ahead and fenced
-// so the live register set stays within two waves per SIMD.  The fold of dim
-// tile dt-1 is issued after the MFMAs of tile dt so the VALU work overlaps the
-// matrix core.  No atomics and no split of a block across workgroups, so
-// nothing depends on scheduling.
+// loads and read by all waves.
+//
+// Per wave and block there are four phases:
+//   scores   S^T = K Q^T                      (matrix cores, K from LDS)
+//   softmax  mask, max, p, sum, bf16 P        (vector ALU)
+//   pv       acc_b = V^T P^T per dim tile     (matrix cores, V from LDS)
+//   fold     O_b = acc_b / l_b into the running state (vector ALU)
+// with the operations of core.hpp.  In fused mode the waves 0-3 (one per
+// SIMD) run the phases in that order and waves 4-7 run them one phase
+// later, with a workgroup barrier between phases: while one wave of a SIMD
+// is in a matrix-core phase the other is in a vector phase, so the two
+// units work at the same time.  LDS holds two blocks (double buffer); the
+// loads of block b+1 are issued when block b starts and waited for before
+// the last barrier of block b.  The per-block step takes the buffer being
+// read and the buffer being filled as restrict pointers, so the compiler
+// knows they do not overlap and never stalls an LDS read on the in-flight
+// loads (it would otherwise wait for every outstanding direct load before
+// the first read).  No atomics and no split of a block across workgroups,
+// so nothing depends on scheduling.
 #include "kernels.hpp"
 #include "tile.hpp"
 
@@ -29,102 +36,278 @@ namespace {
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 
-// Block softmax state of one wave for one staged block.
+// ---------------------------------------------------------------- phases --
+
+// S^T = K Q^T for one staged block: NKT sub-tiles of 32 keys x 32 queries.
+// K fragments are read one head-dim step ahead.
+template <int BK>
+__device__ __forceinline__ void block_scores(const char* kreg, const bf16x8 (&qf)[kDSteps], f32x16 (&s)[BK / 32]) {
+  constexpr int NKT = BK / 32;
+  const KReads<BK> kr(kreg);
+#pragma unroll
+  for (int kt = 0; kt < NKT; ++kt) s[kt] = f32x16{};
+  bf16x8 kf[2][NKT];
+#pragma unroll
+  for (int kt = 0; kt < NKT; ++kt) kf[0][kt] = kr.frag(kt, 0);
+#pragma unroll
+  for (int ds = 0; ds < kDSteps; ++ds) {
+    if (ds + 1 < kDSteps) {
+#pragma unroll
+      for (int kt = 0; kt < NKT; ++kt) kf[(ds + 1) & 1][kt] = kr.frag(kt, ds + 1);
+    }
+#pragma unroll
+    for (int kt = 0; kt < NKT; ++kt) s[kt] = mfma(kf[ds & 1][kt], qf[ds], s[kt]);
+    sched_fence();
+  }
+}
+
+// The same with the Q B-fragments read from LDS: step ds of this lane at
+// qlane + ds*1024 (the wave's 8 KiB Q tile stored in fragment order).
+template <int BK>
+__device__ __forceinline__ void block_scores_q(const char* kreg, const char* qlane, f32x16 (&s)[BK / 32]) {
+  constexpr int NKT = BK / 32;
+  const KReads<BK> kr(kreg);
+#pragma unroll
+  for (int kt = 0; kt < NKT; ++kt) s[kt] = f32x16{};
+  bf16x8 kf[2][NKT];
+  bf16x8 qf[2];
+#pragma unroll
+  for (int kt = 0; kt < NKT; ++kt) kf[0][kt] = kr.frag(kt, 0);
+  qf[0] = as_bf16x8(*reinterpret_cast<const u32x4*>(qlane));
+#pragma unroll
+  for (int ds = 0; ds < kDSteps; ++ds) {
+    if (ds + 1 < kDSteps) {
+#pragma unroll
+      for (int kt = 0; kt < NKT; ++kt) kf[(ds + 1) & 1][kt] = kr.frag(kt, ds + 1);
+      qf[(ds + 1) & 1] = as_bf16x8(*reinterpret_cast<const u32x4*>(qlane + (ds + 1) * 1024));
+    }
+#pragma unroll
+    for (int kt = 0; kt < NKT; ++kt) s[kt] = mfma(kf[ds & 1][kt], qf[ds & 1], s[kt]);
+    sched_fence();
+  }
+}
+
+// Softmax result of one block for one wave: P as MFMA B-fragments per
+// 16-key step, and the block scalars.
 template <int BK, bool F32>
-struct BlockCore {
+struct BlockP {
   static constexpr int NKT = BK / 32;
-  u32x4 ph[NKT][2];  // P (bf16 hi) as B-fragments per 16-key step
-  u32x4 pl[NKT][2];  // P residual (bf16 lo), fp32-output mode only
+  u32x4 ph[NKT][2];  // P rounded to bf16
+  u32x4 pl[NKT][2];  // P - bf16(P) rounded to bf16 (fp32-output mode only)
   float m_t;         // block max, log2 domain (-inf: no visible key)
   float l_b;         // block sum of p
+};
 
-  // S^T, mask, max, p = 2^fma(s, c, -m), canonical sum, bf16 P.
-  // Positions are 32-bit (sequence lengths stay below 2^31).
-  __device__ __forceinline__ void softmax(const char* lds, const bf16x8 (&qf)[kDSteps], int key0, int kv_len,
-                                          int causal, int qpos, bool need_mask, float c) {
-    const int lane = threadIdx.x & 63;
-    const int col = lane & 31;
-    const int half = lane >> 5;
-    f32x16 s[NKT];
+// Causal / kv_len mask of a score block (only for blocks on the causal
+// diagonal or past kv_len): key = key0 + 4*half + kt*32 + 8*(v/4) + v%4 is
+// visible iff key <= limit; masked scores become -inf.  Positions are
+// 32-bit (sequence lengths stay below 2^31).
+template <int BK>
+__device__ __forceinline__ void apply_mask(f32x16 (&s)[BK / 32], int key0, int kv_len, int causal, int qpos) {
+  constexpr int NKT = BK / 32;
+  const int half = (threadIdx.x & 63) >> 5;
+  const int limit = causal ? min(kv_len - 1, qpos) : kv_len - 1;
+  const int room = limit - (key0 + 4 * half);
 #pragma unroll
-    for (int kt = 0; kt < NKT; ++kt) s[kt] = f32x16{};
-    bf16x8 kf[2][NKT];
+  for (int kt = 0; kt < NKT; ++kt) {
 #pragma unroll
-    for (int kt = 0; kt < NKT; ++kt) kf[0][kt] = k_frag<BK>(lds, kt, 0, col, half);
-#pragma unroll
-    for (int ds = 0; ds < kDSteps; ++ds) {
-      if (ds + 1 < kDSteps) {
-#pragma unroll
-        for (int kt = 0; kt < NKT; ++kt) kf[(ds + 1) & 1][kt] = k_frag<BK>(lds, kt, ds + 1, col, half);
-      }
-#pragma unroll
-      for (int kt = 0; kt < NKT; ++kt) s[kt] = mfma(kf[ds & 1][kt], qf[ds], s[kt]);
-      sched_fence();
+    for (int v = 0; v < 16; ++v) {
+      const int off = kt * 32 + 8 * (v >> 2) + (v & 3);
+      s[kt][v] = off <= room ? s[kt][v] : kNegInf;
     }
-    float mx = kNegInf;
-    if (need_mask) {  // wave-uniform: only blocks on the causal diagonal or past kv_len
-      const int kbase = key0 + 4 * half;
-#pragma unroll
-      for (int kt = 0; kt < NKT; ++kt) {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int key = kbase + kt * 32 + 8 * (v >> 2) + (v & 3);
-          const bool ok = key < kv_len && (!causal || key <= qpos);
-          s[kt][v] = ok ? s[kt][v] : kNegInf;
-          mx = fmaxf(mx, s[kt][v]);
-        }
-      }
-    } else {
-#pragma unroll
-      for (int kt = 0; kt < NKT; ++kt) {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kt][v]);
-      }
-    }
-    mx = fmaxf(mx, partner(mx));
-    m_t = block_m(mx, c);
-    const float mu = block_m_use(m_t);
-    float sub[NKT];
-#pragma unroll
-    for (int kt = 0; kt < NKT; ++kt) {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) s[kt][v] = block_p(s[kt][v], c, mu);
-      const float a = tree16(s[kt]);
-      sub[kt] = a + partner(a);
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const float p0 = s[kt][8 * st + 2 * w];
-          const float p1 = s[kt][8 * st + 2 * w + 1];
-          const uint32_t h = pack_bf16(p0, p1);
-          ph[kt][st][w] = h;
-          if constexpr (F32) pl[kt][st][w] = pack_bf16(p0 - bf16_lo_to_f32(h), p1 - bf16_hi_to_f32(h));
-        }
-      }
-    }
-    l_b = combine_subtiles<NKT>(sub);
   }
+}
 
-  // Issue the PV MFMAs of output dim tile dt (chain over the block's keys in
-  // 16-key steps from zero); V fragments prefetched one step ahead.
-  __device__ __forceinline__ f32x16 pv(const char* lds, int dt) const {
-    f32x16 acc = f32x16{};
-    constexpr int NS = NKT * 2;
-    bf16x8 vf[2];
-    const char* vbase = lds + TileLayout<BK>::kKBytes;
-    vf[0] = v_frag<BK>(vbase, dt, 0, 0);
+// Block max (log2 domain) of a masked score block.
+template <int BK>
+__device__ __forceinline__ float block_max(const f32x16 (&s)[BK / 32], float c) {
+  float mx = kNegInf;
+#pragma unroll
+  for (int kt = 0; kt < BK / 32; ++kt) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kt][v]);
+  }
+  return block_m(pair_max(mx), c);
+}
+
+// p = 2^fma(s, c, -m), canonical sum, bf16 P of a masked score block.
+template <int BK, bool F32>
+__device__ __forceinline__ void softmax_core(f32x16 (&s)[BK / 32], float c, BlockP<BK, F32>& P) {
+  constexpr int NKT = BK / 32;
+  P.m_t = block_max<BK>(s, c);
+  const float mu = block_m_use(P.m_t);
+  float sub[NKT];
+#pragma unroll
+  for (int kt = 0; kt < NKT; ++kt) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) s[kt][v] = block_p(s[kt][v], c, mu);
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float p0 = s[kt][8 * st + 2 * w];
+        const float p1 = s[kt][8 * st + 2 * w + 1];
+        const uint32_t h = pack_bf16(p0, p1);
+        P.ph[kt][st][w] = h;
+        if constexpr (F32) P.pl[kt][st][w] = pack_bf16(p0 - bf16_lo_to_f32(h), p1 - bf16_hi_to_f32(h));
+      }
+    }
+    sub[kt] = pair_sum(tree16(s[kt]));
+  }
+  P.l_b = combine_subtiles<NKT>(sub);
+}
+
+template <int BK, bool F32>
+__device__ __forceinline__ void block_softmax(f32x16 (&s)[BK / 32], bool need_mask, int key0, int kv_len, int causal,
+                                              int qpos, float c, BlockP<BK, F32>& P) {
+  if (need_mask) apply_mask<BK>(s, key0, kv_len, causal, qpos);  // wave-uniform
+  softmax_core<BK, F32>(s, c, P);
+}
+
+// One output dim tile of the block: acc_b tile = V^T P^T, an MFMA chain
+// over the block's 16-key steps from zero.  V fragments come from a ring of
+// R registers filled R-1 MFMAs ahead; the ring runs on across tiles when the
+// caller passes the same ring to consecutive tiles.
+template <int BK, bool F32, int R>
+struct VRing {
+  static constexpr int NS = BK / 16;  // 16-key steps per tile
+  static constexpr int N = NS * kDTiles;
+  bf16x8 f[R];
+  __device__ __forceinline__ static bf16x8 load(const VReads<BK>& vr, int i) {
+    const int n = i % NS;
+    return vr.frag(i / NS, n >> 1, n & 1);
+  }
+  __device__ __forceinline__ void start(const VReads<BK>& vr) {
+#pragma unroll
+    for (int i = 0; i < R - 1; ++i) f[i] = load(vr, i);
+  }
+  // MFMAs of tile dt (global MFMA index i = dt*NS + n).
+  __device__ __forceinline__ f32x16 tile(const VReads<BK>& vr, const BlockP<BK, F32>& P, int dt) {
+    f32x16 ab = f32x16{};
 #pragma unroll
     for (int n = 0; n < NS; ++n) {
-      if (n + 1 < NS) vf[(n + 1) & 1] = v_frag<BK>(vbase, dt, (n + 1) >> 1, (n + 1) & 1);
-      const int kt = n >> 1, st = n & 1;
-      acc = mfma(vf[n & 1], as_bf16x8(ph[kt][st]), acc);
-      if constexpr (F32) acc = mfma(vf[n & 1], as_bf16x8(pl[kt][st]), acc);
+      const int i = dt * NS + n;
+      const int j = i + R - 1;
+      if (j < N) f[j % R] = load(vr, j);
+      ab = mfma(f[i % R], as_bf16x8(P.ph[n >> 1][n & 1]), ab);
+      if constexpr (F32) ab = mfma(f[i % R], as_bf16x8(P.pl[n >> 1][n & 1]), ab);
       sched_fence();
     }
-    return acc;
+    return ab;
   }
 };
+
+// Fold of one block item into the running state (core.hpp): the acc * alpha
+// multiply is skipped when no lane of the wave moves its reference (alpha is
+// then 1 on every lane and the multiply exact).
+struct FoldIn {
+  float r;      // 1 / l_b (0 for an empty row)
+  FoldStep f;
+  bool any_move;
+};
+
+__device__ __forceinline__ FoldIn fold_prepare(FoldState& fs, float m_t, float l_b) {
+  const ItemScalars sc = item_scalars(m_t, l_b);
+  FoldIn in;
+  in.r = sc.r;
+  in.f = fold_scalars(fs, sc.L);
+  in.any_move = __any(in.f.move);
+  return in;
+}
+
+__device__ __forceinline__ void fold_tile(f32x16& acc, const f32x16& ab, const FoldIn& in) {
+#pragma unroll
+  for (int v = 0; v < 16; ++v) acc[v] = fold_elem_nomove(in.f, acc[v], ab[v] * in.r);
+}
+
+// PV of the block fused with its fold: tile dt's MFMAs are issued, then tile
+// dt-1 (already finished) is folded while they run.
+template <int BK, bool F32>
+__device__ __forceinline__ void block_pv_fold(const VReads<BK>& vr, const BlockP<BK, F32>& P, const FoldIn& in,
+                                              f32x16 (&acc)[kDTiles]) {
+  if (in.any_move) {
+#pragma unroll
+    for (int dt = 0; dt < kDTiles; ++dt) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[dt][v] = acc[dt][v] * in.f.alpha;
+    }
+  }
+  VRing<BK, F32, 3> ring;
+  ring.start(vr);
+  f32x16 ab0 = ring.tile(vr, P, 0);
+  f32x16 ab1 = ring.tile(vr, P, 1);
+  fold_tile(acc[0], ab0, in);
+  sched_fence();
+  ab0 = ring.tile(vr, P, 2);
+  fold_tile(acc[1], ab1, in);
+  sched_fence();
+  ab1 = ring.tile(vr, P, 3);
+  fold_tile(acc[2], ab0, in);
+  fold_tile(acc[3], ab1, in);
+}
+
+// The vector stage of the software-pipelined kernel: the softmax of block j
+// (scores s, already masked) runs on the vector ALU while the matrix cores
+// run the PV MFMAs of block j-1, dim tile by dim tile; each tile is folded
+// into the running state as soon as its MFMA chain ends.  The work is cut
+// into slots of one PV MFMA each; a slot also computes two softmax elements
+// (p, their bf16 pair and the canonical sum tree as its operands complete),
+// and slots are fenced so the scheduler cannot bunch the MFMAs together.
+// The arithmetic is exactly that of softmax_core and block_pv_fold.
+template <int BK>
+__device__ __forceinline__ void pipe_stage(f32x16 (&s)[BK / 32], float c, BlockP<BK, false>& Pn,
+                                           const VReads<BK>& vr, const BlockP<BK, false>& Pp, const FoldIn& inp,
+                                           f32x16 (&acc)[kDTiles]) {
+  constexpr int NKT = BK / 32;
+  constexpr int NS = BK / 16;      // 16-key steps (MFMAs) per dim tile
+  constexpr int N = NS * kDTiles;  // slots
+  static_assert(2 * N == 16 * NKT, "two softmax elements per slot");
+  Pn.m_t = block_max<BK>(s, c);
+  const float mu = block_m_use(Pn.m_t);
+  float sub[NKT];                // canonical sum of each sub-tile
+  float lv1 = 0.0f, lv2 = 0.0f;  // pending first / second tree level
+  VRing<BK, false, 2> ring;
+  ring.start(vr);
+  f32x16 ab;
+  sched_fence();
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const int t = i / NS;
+    const int n = i % NS;
+    const int j = i + 1;
+    if (j < N) ring.f[j % 2] = ring.load(vr, j);
+    ab = mfma(ring.f[i % 2], as_bf16x8(Pp.ph[n >> 1][n & 1]), n == 0 ? f32x16{} : ab);
+    // softmax elements 2i, 2i+1 (pair wp of sub-tile kt); the sum tree of
+    // tree16 is reduced as its operands complete
+    const int kt = (2 * i) / 16;
+    const int v = (2 * i) % 16;
+    const int wp = v / 2;
+    const float p0 = block_p(s[kt][v], c, mu);
+    const float p1 = block_p(s[kt][v + 1], c, mu);
+    Pn.ph[kt][v / 8][(v % 8) / 2] = pack_bf16(p0, p1);
+    const float a = p0 + p1;
+    if ((wp & 1) == 0) {
+      lv1 = a;
+    } else {
+      const float b = lv1 + a;
+      if ((wp & 3) == 1) {
+        lv2 = b;
+      } else {
+        const float cc = lv2 + b;
+        if (wp == 3) {
+          sub[kt] = cc;
+        } else {
+          sub[kt] = pair_sum(sub[kt] + cc);
+        }
+      }
+    }
+    if (n == NS - 1) fold_tile(acc[t], ab, inp);  // tile t complete
+    sched_fence();
+  }
+  Pn.l_b = combine_subtiles<NKT>(sub);
+}
+
+// ------------------------------------------------------------ work map --
 
 struct TileMap {
   int b, hk, head, t0, t, tile_t1, t_last;
@@ -146,177 +329,350 @@ __device__ __forceinline__ TileMap map_tile(const PrefillArgs& a, int64_t wg) {
   const int tile_rows = 32 * a.pos_groups;
   const int tile_t0 = ptile * tile_rows;
   m.tile_t1 = min(a.Sq, tile_t0 + tile_rows) - 1;
+  const bool wave_used = wave < a.heads_per_wg * a.pos_groups;  // 8 % G != 0 leaves waves idle
   m.head = m.hk * a.G + hs * a.heads_per_wg + (wave % a.heads_per_wg);
   m.t0 = tile_t0 + 32 * (wave / a.heads_per_wg);
   m.t = m.t0 + col;
-  m.q_ok = m.t < a.Sq;
+  m.wave_has_rows = wave_used && m.t0 < a.Sq;
+  m.q_ok = m.wave_has_rows && m.t < a.Sq;
   m.qpos = a.pos0 + m.t;
   m.t_last = min(a.Sq, m.t0 + 32) - 1;
-  m.wave_has_rows = m.t0 < a.Sq;
   return m;
 }
 
-// One fold step of output dim tile dt (acc_b -> O_b -> running acc).  When
-// every lane of the wave takes the "add" step (the common case) the select
-// of fold_elem is skipped; the arithmetic is the same.
-__device__ __forceinline__ void fold_tile(f32x16& acc, const f32x16& ab, const ItemScalars& sc, const FoldStep& f,
-                                          bool all_add) {
-  if (all_add) {
+// Common per-wave set-up of both kernels.
+struct WaveCtx {
+  TileMap tm;
+  __amdgpu_buffer_rsrc_t krs;  // keys [0, kv_len) of this kv head
+  __amdgpu_buffer_rsrc_t vrs;
+  int64_t row_stride;
+  bf16x8 qf[kDSteps];
+};
+
+__device__ __forceinline__ void wave_setup(const PrefillArgs& a, int64_t wg, WaveCtx& w) {
+  const int half = (threadIdx.x & 63) >> 5;
+  w.tm = map_tile(a, wg);
+  const int64_t kvoff = static_cast<int64_t>(w.tm.b) * a.kv_bstride + static_cast<int64_t>(w.tm.hk) * kHeadDim;
+  w.row_stride = static_cast<int64_t>(a.Hkv) * kHeadDim;
+  w.krs = head_rsrc(a.k + kvoff, a.kv_len, static_cast<int>(w.row_stride * 2));
+  w.vrs = head_rsrc(a.v + kvoff, a.kv_len, static_cast<int>(w.row_stride * 2));
+  const uint16_t* qrow = a.q + static_cast<int64_t>(w.tm.b) * a.q_bstride +
+                         (static_cast<int64_t>(w.tm.t) * a.Hq + w.tm.head) * kHeadDim + 8 * half;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) acc[v] = fold_add(acc[v], item_out(ab[v], sc), f.beta);
-  } else {
-#pragma unroll
-    for (int v = 0; v < 16; ++v) acc[v] = fold_elem(f, acc[v], item_out(ab[v], sc));
-  }
+  for (int ds = 0; ds < kDSteps; ++ds)
+    w.qf[ds] = as_bf16x8(w.tm.q_ok ? gload16(qrow + 16 * ds) : u32x4{0, 0, 0, 0});
 }
 
-template <int BK, bool F32, bool EMIT>
-__global__ __launch_bounds__(kThreads) void prefill_kernel(const PrefillArgs a) {
-  using L = TileLayout<BK>;
-  constexpr int NBUF = EMIT ? 1 : 2;
-  __shared__ __attribute__((aligned(16))) char lds[NBUF * L::kBytes];
+// Does block blk hold a key some row of this wave may see?
+template <int BK>
+__device__ __forceinline__ bool wave_sees(const PrefillArgs& a, const TileMap& tm, int64_t blk) {
+  return tm.wave_has_rows && blk * BK < a.kv_len && (!a.causal || blk * BK <= a.pos0 + tm.t_last);
+}
+// Is every key of block blk visible to every row of this wave?
+template <int BK>
+__device__ __forceinline__ bool wave_full(const PrefillArgs& a, const TileMap& tm, int64_t blk) {
+  return (blk + 1) * BK <= a.kv_len && (!a.causal || (blk + 1) * BK - 1 <= a.pos0 + tm.t0);
+}
 
-  const int lane = threadIdx.x & 63;
-  const int half = lane >> 5;
+// ----------------------------------------------------------- fused mode --
 
-  int64_t wg = blockIdx.x;
-  int pidx = 0;
-  if constexpr (EMIT) {
-    pidx = static_cast<int>(wg % a.n_emit);
-    wg /= a.n_emit;
-  }
-  const TileMap tm = map_tile(a, wg);
-
-  const uint16_t* kb = a.k + static_cast<int64_t>(tm.b) * a.kv_bstride + static_cast<int64_t>(tm.hk) * kHeadDim;
-  const uint16_t* vb = a.v + static_cast<int64_t>(tm.b) * a.kv_bstride + static_cast<int64_t>(tm.hk) * kHeadDim;
-  const int64_t row_stride = static_cast<int64_t>(a.Hkv) * kHeadDim;
-
-  bf16x8 qf[kDSteps];
-  {
-    const uint16_t* qrow = a.q + static_cast<int64_t>(tm.b) * a.q_bstride +
-                           (static_cast<int64_t>(tm.t) * a.Hq + tm.head) * kHeadDim + 8 * half;
-#pragma unroll
-    for (int ds = 0; ds < kDSteps; ++ds)
-      qf[ds] = as_bf16x8(tm.q_ok ? gload16(qrow + 16 * ds) : u32x4{0, 0, 0, 0});
-  }
-
-  // Does block blk hold a key some row of this wave may see?
-  auto wave_sees = [&](int64_t blk) {
-    return tm.wave_has_rows && blk * BK < a.kv_len && (!a.causal || blk * BK <= a.pos0 + tm.t_last);
-  };
-  // Is every key of block blk visible to every row of this wave?
-  auto wave_full = [&](int64_t blk) {
-    return (blk + 1) * BK <= a.kv_len && (!a.causal || (blk + 1) * BK - 1 <= a.pos0 + tm.t0);
-  };
+// Epilogue of both fused kernels: O = acc / l, LSE.
+template <bool F32>
+__device__ __forceinline__ void write_out(const PrefillArgs& a, const TileMap& tm, const FoldState& fs,
+                                          const f32x16 (&acc)[kDTiles]) {
+  const int half = (threadIdx.x & 63) >> 5;
+  const Final fin = finalize(fs);
   const int64_t out_row = static_cast<int64_t>(tm.b) * a.Sq + tm.t;  // row index in [B*Sq]
-
-  if constexpr (EMIT) {
-    const int64_t blk = a.emit_blocks[pidx];
-    const bool tile_sees = blk * BK < a.kv_len && (!a.causal || blk * BK <= a.pos0 + tm.tile_t1);
-    const bool active = tile_sees && wave_sees(blk);
-    BlockCore<BK, F32> bc;
-    if (tile_sees) {
-      BlockLoader<BK, kWaves> ld;
-      ld.init(static_cast<int>(row_stride));
-      ld.issue(lds, kb, vb, row_stride, blk * BK, a.kv_len);
-      wait_direct_loads();
-      __syncthreads();
-      if (active)
-        bc.softmax(lds, qf, static_cast<int>(blk * BK), static_cast<int>(a.kv_len), a.causal,
-                   static_cast<int>(tm.qpos), !wave_full(blk), a.c);
-    }
-    const ItemScalars sc = active ? item_scalars(bc.m_t, bc.l_b) : ItemScalars{0.0f, kNegInf};
-    const int64_t prow = static_cast<int64_t>(pidx) * a.B * a.Sq + out_row;
-    float* po = a.part_out + (prow * a.Hq + tm.head) * kHeadDim;
+  const int64_t orow = (out_row * a.Hq + tm.head) * kHeadDim;
 #pragma unroll
-    for (int dt = 0; dt < kDTiles; ++dt) {
-      const f32x16 ob = active ? bc.pv(lds, dt) : f32x16{};
-      if (tm.q_ok) {
+  for (int dt = 0; dt < kDTiles; ++dt) {
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int d = dt * 32 + 8 * g + 4 * half;
-          *reinterpret_cast<f32x4*>(po + d) = f32x4{item_out(ob[4 * g], sc), item_out(ob[4 * g + 1], sc),
-                                                    item_out(ob[4 * g + 2], sc), item_out(ob[4 * g + 3], sc)};
-        }
+    for (int g = 0; g < 4; ++g) {
+      const int d = dt * 32 + 8 * g + 4 * half;
+      const float o0 = acc[dt][4 * g] * fin.r;
+      const float o1 = acc[dt][4 * g + 1] * fin.r;
+      const float o2 = acc[dt][4 * g + 2] * fin.r;
+      const float o3 = acc[dt][4 * g + 3] * fin.r;
+      if constexpr (F32) {
+        *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + orow + d) = f32x4{o0, o1, o2, o3};
+      } else {
+        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + orow + d) =
+            u32x2{pack_bf16(o0, o1), pack_bf16(o2, o3)};
       }
     }
-    if (tm.q_ok && half == 0) a.part_lse[prow * a.Hq + tm.head] = sc.L;
-    return;
-  } else {
-    const int64_t n_kv_blocks = (a.kv_len + BK - 1) / BK;
-    const int64_t last_blk = a.causal ? min(n_kv_blocks - 1, (a.pos0 + tm.tile_t1) / BK) : n_kv_blocks - 1;
-    FoldState fs{kNegInf, 0.0f};
-    f32x16 acc[kDTiles];
-#pragma unroll
-    for (int dt = 0; dt < kDTiles; ++dt) acc[dt] = f32x16{};
-
-    BlockLoader<BK, kWaves> ld;
-    ld.init(static_cast<int>(row_stride));
-    if (last_blk >= 0) ld.issue(lds, kb, vb, row_stride, 0, a.kv_len);
-    wait_direct_loads();
-    __syncthreads();
-
-    for (int64_t blk = 0; blk <= last_blk; ++blk) {
-      const char* cur = lds + (blk & 1) * L::kBytes;
-      if (blk + 1 <= last_blk)
-        ld.issue(lds + ((blk + 1) & 1) * L::kBytes, kb, vb, row_stride, (blk + 1) * BK, a.kv_len);
-      if (wave_sees(blk)) {
-        BlockCore<BK, F32> bc;
-        bc.softmax(cur, qf, static_cast<int>(blk * BK), static_cast<int>(a.kv_len), a.causal,
-                   static_cast<int>(tm.qpos), !wave_full(blk), a.c);
-        const ItemScalars sc = item_scalars(bc.m_t, bc.l_b);
-        const FoldStep f = fold_scalars(fs, sc.L);
-        const bool all_add = __all(f.mode == kFoldAdd);
-        f32x16 ab0 = bc.pv(cur, 0);
-        f32x16 ab1 = bc.pv(cur, 1);
-        fold_tile(acc[0], ab0, sc, f, all_add);
-        ab0 = bc.pv(cur, 2);
-        fold_tile(acc[1], ab1, sc, f, all_add);
-        ab1 = bc.pv(cur, 3);
-        fold_tile(acc[2], ab0, sc, f, all_add);
-        fold_tile(acc[3], ab1, sc, f, all_add);
-      }
-      wait_direct_loads();
-      __syncthreads();
-    }
-
-    if (!tm.q_ok) return;
-    const Final fin = finalize(fs);
-    const int64_t orow = (out_row * a.Hq + tm.head) * kHeadDim;
-#pragma unroll
-    for (int dt = 0; dt < kDTiles; ++dt) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d = dt * 32 + 8 * g + 4 * half;
-        const float o0 = acc[dt][4 * g] * fin.r;
-        const float o1 = acc[dt][4 * g + 1] * fin.r;
-        const float o2 = acc[dt][4 * g + 2] * fin.r;
-        const float o3 = acc[dt][4 * g + 3] * fin.r;
-        if constexpr (F32) {
-          *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + orow + d) = f32x4{o0, o1, o2, o3};
-        } else {
-          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + orow + d) =
-              u32x2{pack_bf16(o0, o1), pack_bf16(o2, o3)};
-        }
-      }
-    }
-    if (half == 0) a.lse[out_row * a.Hq + tm.head] = fin.lse;
   }
+  if (half == 0) a.lse[out_row * a.Hq + tm.head] = fin.lse;
+}
+
+// bf16 output: software-pipelined over blocks.  Iteration j has two stages,
+// each ended by a workgroup barrier:
+//   matrix stage: S_j = K_j Q^T
+//   vector stage: softmax of S_j (vector ALU) interleaved with the PV MFMAs
+//                 and the fold of block j-1 (pipe_stage)
+// so the PV work of every block hides under the softmax of the next one.
+// Registers are the limit (two waves per SIMD, 256 each), so the Q tile of
+// each wave lives in LDS in fragment order (8 KiB per wave, read once per
+// block), K is single-buffered and V double-buffered: LDS holds K_j, V_{j-1},
+// V_j and Q (160 KiB for 128-key blocks).  V_j is loaded from the start of
+// iteration j (its buffer held V_{j-2}) and must land by the vector stage of
+// iteration j+1; K_{j+1} is loaded once every wave has read K_j (the vector
+// stage of iteration j) and must land by the end of that iteration.  The
+// step takes the regions as restrict pointers, so the compiler does not
+// stall LDS reads of one region on the in-flight loads into another.
+template <int BK>
+__global__ __launch_bounds__(kThreads) void prefill_pipe_kernel(const PrefillArgs a) {
+  using L = TileLayout<BK>;
+  using Ld = BlockLoader<BK, kWaves>;
+  using P = BlockP<BK, false>;
+  __shared__ __attribute__((aligned(16))) char kbuf[L::kKBytes];
+  __shared__ __attribute__((aligned(16))) char vbuf[2 * L::kVBytes];
+  __shared__ __attribute__((aligned(16))) char qbuf[kWaves * 32 * kHeadDim * 2];
+
+  WaveCtx w;
+  wave_setup(a, blockIdx.x, w);
+  const TileMap& tm = w.tm;
+  const int64_t n_kv_blocks = (a.kv_len + BK - 1) / BK;
+  const int64_t nblk = a.causal ? min(n_kv_blocks, (a.pos0 + tm.tile_t1) / BK + 1) : n_kv_blocks;
+
+  FoldState fs{kNegInf, 0.0f};
+  f32x16 acc[kDTiles];
+#pragma unroll
+  for (int dt = 0; dt < kDTiles; ++dt) acc[dt] = f32x16{};
+
+  Ld ld;
+  ld.init(static_cast<int>(w.row_stride));
+  // this lane's Q fragments, step ds at qlane + ds*1024
+  char* const qlane = qbuf + ld.wave * (32 * kHeadDim * 2) + (threadIdx.x & 63) * 16;
+#pragma unroll
+  for (int ds = 0; ds < kDSteps; ++ds) *reinterpret_cast<u32x4*>(qlane + ds * 1024) = __builtin_bit_cast(u32x4, w.qf[ds]);
+  // V buffer 1 stands for block -1 in the first step: zeros
+  for (int i = threadIdx.x; i < L::kVBytes / 16; i += kThreads)
+    *reinterpret_cast<u32x4*>(vbuf + L::kVBytes + 16 * i) = u32x4{0, 0, 0, 0};
+  if (nblk > 0) ld.issue_k(kbuf, w.krs, 0);
+  wait_direct_loads();  // K_0
+  lds_barrier();
+
+  const int kvl = static_cast<int>(a.kv_len);
+  const int qpos = static_cast<int>(tm.qpos);
+  auto cnt = [&](int64_t blk) { return blk < nblk ? Ld::NI : 0; };
+
+  // kc: K_j (read, then refilled with K_{j+1}); vn: V buffer refilled with
+  // V_j; vp: V_{j-1} (read).  Pn/inn: softmax result of block j; Pp/inp: that
+  // of block j-1 (pending pv+fold when pend).
+  auto step = [&](int64_t blk, char* __restrict__ kc, char* __restrict__ vn, const char* __restrict__ vp, P& Pn,
+                  FoldIn& inn, const P& Pp, const FoldIn& inp, bool& pend) {
+    if (blk < nblk) ld.issue_v(vn, w.vrs, blk * BK);
+    const bool sm = blk < nblk && wave_sees<BK>(a, tm, blk);
+    f32x16 s[BK / 32];
+    if (sm) block_scores_q<BK>(kc, qlane, s);
+    const VReads<BK> vr(vp);  // addresses for the vector stage, computed while the MFMAs run
+    sched_fence();
+    wait_loads_leq<Ld::NI>(cnt(blk));  // V_{j-1} landed (V_j may be in flight)
+    lds_barrier();
+    if (blk + 1 < nblk) ld.issue_k(kc, w.krs, (blk + 1) * BK);
+    if (sm && !wave_full<BK>(a, tm, blk)) apply_mask<BK>(s, static_cast<int>(blk * BK), kvl, a.causal, qpos);
+    if (pend && inp.any_move) {
+#pragma unroll
+      for (int dt = 0; dt < kDTiles; ++dt) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[dt][v] = acc[dt][v] * inp.f.alpha;
+      }
+    }
+    if (sm || pend) {
+      // One code path for every case: without a block j the scores are all
+      // -inf (p = 0, result unused); without a block j-1 the pending state is
+      // all zero (P = 0, r = beta = 0) and its V buffer holds zeros, so the
+      // fold adds exact zeros.
+      if (!sm) {
+#pragma unroll
+        for (int kt = 0; kt < BK / 32; ++kt) {
+#pragma unroll
+          for (int v = 0; v < 16; ++v) s[kt][v] = kNegInf;
+        }
+      }
+      pipe_stage<BK>(s, a.c, Pn, vr, Pp, inp, acc);
+    }
+    if (sm) {
+      inn = fold_prepare(fs, Pn.m_t, Pn.l_b);
+    } else {
+      Pn = P{};  // keeps the dead state out of the live range
+      inn = FoldIn{};
+    }
+    pend = sm;
+    sched_fence();
+    wait_direct_loads();  // K_{j+1} (and V_j) landed
+    lds_barrier();
+  };
+
+  P PA{}, PB{};
+  FoldIn ia{}, ib{};
+  bool pend = false;
+  for (int64_t blk = 0; blk <= nblk; ++blk) {
+    const int cb = static_cast<int>(blk & 1);
+    step(blk, kbuf, vbuf + cb * L::kVBytes, vbuf + (cb ^ 1) * L::kVBytes, PA, ia, PB, ib, pend);
+    PB = PA;  // block j becomes the pending block
+    ib = ia;
+  }
+
+  if (!tm.q_ok) return;
+  write_out<false>(a, tm, fs, acc);
+}
+
+// fp32 output (P carried as bf16 hi + lo, two MFMAs per key step): the
+// phases run one after the other, one barrier after each.  K_{j+2} is loaded
+// into the K buffer of block j in the third phase of block j and V_{j+1}
+// into the other V buffer in the second phase, so each load has about four
+// phases to land.
+template <int BK, bool F32>
+__global__ __launch_bounds__(kThreads) void prefill_fused_kernel(const PrefillArgs a) {
+  using L = TileLayout<BK>;
+  using Ld = BlockLoader<BK, kWaves>;
+  __shared__ __attribute__((aligned(16))) char kbuf[2 * L::kKBytes];
+  __shared__ __attribute__((aligned(16))) char vbuf[2 * L::kVBytes];
+
+  WaveCtx w;
+  wave_setup(a, blockIdx.x, w);
+  const TileMap& tm = w.tm;
+  const int64_t n_kv_blocks = (a.kv_len + BK - 1) / BK;
+  const int64_t nblk = a.causal ? min(n_kv_blocks, (a.pos0 + tm.tile_t1) / BK + 1) : n_kv_blocks;
+
+  FoldState fs{kNegInf, 0.0f};
+  f32x16 acc[kDTiles];
+#pragma unroll
+  for (int dt = 0; dt < kDTiles; ++dt) acc[dt] = f32x16{};
+
+  sched_fence();  // the Q loads of wave_setup stay ahead of the direct loads
+  Ld ld;
+  ld.init(static_cast<int>(w.row_stride));
+  auto cnt = [&](int64_t blk) { return blk < nblk ? Ld::NI : 0; };  // loads of one region of blk
+  if (nblk > 0) {
+    ld.issue_k(kbuf, w.krs, 0);
+    ld.issue_v(vbuf, w.vrs, 0);
+  }
+  if (nblk > 1) ld.issue_k(kbuf + L::kKBytes, w.krs, BK);
+  wait_direct_loads();  // Q, K_0, V_0, K_1
+  lds_barrier();
+
+  const int kvl = static_cast<int>(a.kv_len);
+  const int qpos = static_cast<int>(tm.qpos);
+
+  // kc: K of blk (read, then refilled with blk+2); vc: V of blk; vn: V buffer
+  // being filled with blk+1.  The three do not overlap.
+  auto step = [&](int64_t blk, char* __restrict__ kc, const char* __restrict__ vc, char* __restrict__ vn) {
+    const bool sees = wave_sees<BK>(a, tm, blk);
+    f32x16 s[BK / 32];
+    BlockP<BK, F32> P;
+    if (sees) block_scores<BK>(kc, w.qf, s);
+    sched_fence();
+    lds_barrier();
+    if (blk + 1 < nblk) ld.issue_v(vn, w.vrs, (blk + 1) * BK);
+    FoldIn in{};
+    if (sees) {
+      block_softmax<BK, F32>(s, !wave_full<BK>(a, tm, blk), static_cast<int>(blk * BK), kvl, a.causal, qpos, a.c, P);
+      in = fold_prepare(fs, P.m_t, P.l_b);
+    }
+    sched_fence();
+    wait_loads_leq<Ld::NI>(cnt(blk + 1) + cnt(blk + 1));  // V of blk landed
+    lds_barrier();
+    if (blk + 2 < nblk) ld.issue_k(kc, w.krs, (blk + 2) * BK);
+    if (sees) block_pv_fold<BK, F32>(VReads<BK>(vc), P, in, acc);
+    sched_fence();
+    wait_loads_leq<Ld::NI>(cnt(blk + 1) + cnt(blk + 2));  // K of blk+1 landed
+    lds_barrier();
+  };
+  for (int64_t blk = 0; blk < nblk; ++blk) {
+    const int cb = static_cast<int>(blk & 1);
+    step(blk, kbuf + cb * L::kKBytes, vbuf + cb * L::kVBytes, vbuf + (cb ^ 1) * L::kVBytes);
+  }
+
+  if (!tm.q_ok) return;
+  write_out<F32>(a, tm, fs, acc);
+}
+
+// ------------------------------------------------------------ emit mode --
+
+// One workgroup per (owned block, tile): stage the block, compute its item
+// (O_b, L_b) for every row of the tile and write it.
+template <int BK, bool F32>
+__global__ __launch_bounds__(kThreads) void prefill_emit_kernel(const PrefillArgs a) {
+  using L = TileLayout<BK>;
+  __shared__ __attribute__((aligned(16))) char k0[L::kKBytes];
+  __shared__ __attribute__((aligned(16))) char v0[L::kVBytes];
+
+  const int half = (threadIdx.x & 63) >> 5;
+  int64_t wg = blockIdx.x;
+  const int pidx = static_cast<int>(wg % a.n_emit);
+  wg /= a.n_emit;
+  WaveCtx w;
+  wave_setup(a, wg, w);
+  const TileMap& tm = w.tm;
+
+  const int64_t blk = a.emit_blocks[pidx];
+  const bool tile_sees = blk * BK < a.kv_len && (!a.causal || blk * BK <= a.pos0 + tm.tile_t1);
+  const bool active = tile_sees && wave_sees<BK>(a, tm, blk);
+  f32x16 ab[kDTiles];
+  BlockP<BK, F32> P;
+  if (tile_sees) {  // uniform over the workgroup
+    BlockLoader<BK, kWaves> ld;
+    ld.init(static_cast<int>(w.row_stride));
+    ld.issue_k(k0, w.krs, blk * BK);
+    ld.issue_v(v0, w.vrs, blk * BK);
+    wait_direct_loads();
+    lds_barrier();
+    if (active) {
+      f32x16 s[BK / 32];
+      block_scores<BK>(k0, w.qf, s);
+      block_softmax<BK, F32>(s, !wave_full<BK>(a, tm, blk), static_cast<int>(blk * BK), static_cast<int>(a.kv_len),
+                             a.causal, static_cast<int>(tm.qpos), a.c, P);
+      const VReads<BK> vr(v0);
+      VRing<BK, F32, 3> ring;
+      ring.start(vr);
+#pragma unroll
+      for (int dt = 0; dt < kDTiles; ++dt) ab[dt] = ring.tile(vr, P, dt);
+    }
+  }
+  const ItemScalars sc = active ? item_scalars(P.m_t, P.l_b) : ItemScalars{0.0f, kNegInf};
+  if (!tm.q_ok) return;
+  const int64_t out_row = static_cast<int64_t>(tm.b) * a.Sq + tm.t;
+  const int64_t prow = static_cast<int64_t>(pidx) * a.B * a.Sq + out_row;
+  float* po = a.part_out + (prow * a.Hq + tm.head) * kHeadDim;
+#pragma unroll
+  for (int dt = 0; dt < kDTiles; ++dt) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int d = dt * 32 + 8 * g + 4 * half;
+      f32x4 o = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      if (active)
+        o = f32x4{item_out(ab[dt][4 * g], sc), item_out(ab[dt][4 * g + 1], sc), item_out(ab[dt][4 * g + 2], sc),
+                  item_out(ab[dt][4 * g + 3], sc)};
+      *reinterpret_cast<f32x4*>(po + d) = o;
+    }
+  }
+  if (half == 0) a.part_lse[prow * a.Hq + tm.head] = sc.L;
 }
 
 template <int BK, bool F32, bool EMIT>
 hipError_t launch_t(PrefillArgs a, hipStream_t s) {
-  // tile = 8 column tiles of 32 positions: heads of the group first, then positions
-  a.heads_per_wg = a.G < kWaves ? a.G : kWaves;
-  a.pos_groups = kWaves / a.heads_per_wg;
-  a.hsubs = a.G / a.heads_per_wg;
+  // tile = up to 8 column tiles of 32 positions: heads of the group first
+  // (the largest divisor of G that fits), then positions
+  int hpw = a.G < kWaves ? a.G : kWaves;
+  while (a.G % hpw != 0) --hpw;
+  a.heads_per_wg = hpw;
+  a.pos_groups = kWaves / hpw;
+  a.hsubs = a.G / hpw;
   const int tile_rows = 32 * a.pos_groups;
   a.n_ptiles = (a.Sq + tile_rows - 1) / tile_rows;
   int64_t grid = static_cast<int64_t>(a.n_ptiles) * a.B * a.Hkv * a.hsubs;
   if (EMIT) grid *= a.n_emit;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((prefill_kernel<BK, F32, EMIT>), dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, s, a);
+  if constexpr (EMIT) {
+    hipLaunchKernelGGL((prefill_emit_kernel<BK, F32>), dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, s, a);
+  } else if constexpr (F32) {
+    hipLaunchKernelGGL((prefill_fused_kernel<BK, F32>), dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((prefill_pipe_kernel<BK>), dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -51,12 +51,20 @@ __device__ __forceinline__ void direct_load16(const uint16_t* src, char* lds_dst
 #endif
 }
 
-// Direct global->LDS loads of KV blocks into a tile buffer: the calling wave
-// issues loads wave, wave+NW, ... of each region (1 KiB = 4 key rows each).
-// The lane's element offsets within a block are fixed, so they are computed
-// once; a block that reaches past kv_len takes the clamped path, where rows
-// past kv_len load the last valid key instead (always masked: score -inf,
-// weight exactly 0).
+// Buffer resource over the keys [0, kv_len) of one kv head: key r at byte
+// r * row_bytes.  Reads at or past num_records return zeros, which is how
+// the rows of a block past kv_len are filled (they are always masked: score
+// -inf, weight exactly 0, and 0 * 0 adds nothing).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const uint16_t* base, int64_t kv_len, int row_bytes) {
+  const int64_t bytes = kv_len > 0 ? (kv_len - 1) * row_bytes + kHeadDim * 2 : 0;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), 0, static_cast<int>(bytes), 0x00020000);
+}
+
+// Direct buffer->LDS loads of one KV block into one region: the calling wave
+// issues loads wave, wave+NW, ... (1 KiB = 4 key rows each).  The per-lane
+// offset is fixed (one register); the block and load offsets are uniform
+// (scalar soffset).  Offsets are 32-bit: callers keep kv_len * row_bytes
+// below 2^31.
 template <int BK, int NW>
 struct BlockLoader {
   using L = TileLayout<BK>;
@@ -64,55 +72,64 @@ struct BlockLoader {
   static_assert(L::kLoadsPerRegion % NW == 0, "loads must divide over the waves");
   // Row of load i is r_i = 4*(wave + NW*i) + lane/16; both swizzles depend on
   // r_i only through bits that do not change with i (NW is a multiple of 4),
-  // so offset i is offset 0 plus the uniform stride i * 4*NW rows.
+  // so load i is load 0 moved by the uniform 4*NW*i rows.
   static_assert(NW % 4 == 0, "swizzle bits must not depend on the load index");
-  int koff0;
-  int voff0;
+  int kbyte0;  // lane's byte offset of load 0 within the block (K swizzle)
+  int vbyte0;  // the same with the V swizzle
   int wave;
+  int row_bytes;
 
   __device__ __forceinline__ void init(int row_stride) {
     wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+    row_bytes = row_stride * 2;
     const int lane = threadIdx.x & 63;
     const int p = lane & 15;
     const int r = 4 * wave + (lane >> 4);
-    koff0 = r * row_stride + ((p ^ L::k_swz(r)) << 3);
-    voff0 = r * row_stride + ((p ^ L::v_swz(r)) << 3);
+    kbyte0 = r * row_bytes + ((p ^ L::k_swz(r)) << 4);
+    vbyte0 = r * row_bytes + ((p ^ L::v_swz(r)) << 4);
   }
 
-  __device__ __forceinline__ void issue(char* buf, const uint16_t* kb, const uint16_t* vb, int64_t row_stride,
-                                        int64_t key0, int64_t kv_len) const {
-    if (key0 + BK <= kv_len) {
+  template <bool V>
+  __device__ __forceinline__ void issue(char* dst, __amdgpu_buffer_rsrc_t rs, int64_t key0) const {
+    const int off0 = V ? vbyte0 : kbyte0;
 #pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        const int n = wave + NW * i;
-        const int64_t rows = key0 + 4 * NW * i;  // uniform
-        direct_load16(kb + rows * row_stride + koff0, buf + n * 1024);
-        direct_load16(vb + rows * row_stride + voff0, buf + L::kKBytes + n * 1024);
-      }
-    } else {
-      const int lane = threadIdx.x & 63;
-      const int p = lane & 15;
-#pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        const int n = wave + NW * i;
-        const int r = 4 * n + (lane >> 4);
-        int64_t key = key0 + r;
-        key = key < kv_len ? key : kv_len - 1;
-        direct_load16(kb + key * row_stride + ((p ^ L::k_swz(r)) << 3), buf + n * 1024);
-        direct_load16(vb + key * row_stride + ((p ^ L::v_swz(r)) << 3), buf + L::kKBytes + n * 1024);
-      }
+    for (int i = 0; i < NI; ++i) {
+      const int n = wave + NW * i;
+      const int soff = static_cast<int>(key0 + 4 * NW * i) * row_bytes;  // uniform
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + n * 1024), 16, off0, soff, 0, 0);
     }
   }
+  __device__ __forceinline__ void issue_k(char* dst, __amdgpu_buffer_rsrc_t rs, int64_t key0) const {
+    issue<false>(dst, rs, key0);
+  }
+  __device__ __forceinline__ void issue_v(char* dst, __amdgpu_buffer_rsrc_t rs, int64_t key0) const {
+    issue<true>(dst, rs, key0);
+  }
 };
+
+// Wait until at most n of this wave's vector-memory loads are outstanding
+// (they retire in issue order); n is one of 0, NI, 2*NI of a loader, chosen
+// by a wave-uniform branch so the count stays an immediate.
+template <int NI>
+__device__ __forceinline__ void wait_loads_leq(int n) {
+  static_assert(2 * NI < 64, "vmcnt field");
+  if (n <= 0) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), lgkm/exp untouched
+  } else if (n <= NI) {
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (NI & 15) | ((NI >> 4) << 14));
+  } else {
+    __builtin_amdgcn_s_waitcnt(0x0F70 | ((2 * NI) & 15) | (((2 * NI) >> 4) << 14));
+  }
+}
 
 // Wait until this wave's direct loads have landed in LDS (vmcnt(0)).
 __device__ __forceinline__ void wait_direct_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // A-fragment of K for sub-tile kt, head-dim step ds (lane: key row kt*32+col,
-// dims 16ds + 8*half + 0..7).
+// dims 16ds + 8*half + 0..7).  kreg points at the K region.
 template <int BK>
-__device__ __forceinline__ bf16x8 k_frag(const char* lds, int kt, int ds, int col, int half) {
-  return as_bf16x8(lds_load16(lds, TileLayout<BK>::k_off(kt * 32 + col, 2 * ds + half)));
+__device__ __forceinline__ bf16x8 k_frag(const char* kreg, int kt, int ds, int col, int half) {
+  return as_bf16x8(lds_load16(kreg, TileLayout<BK>::k_off(kt * 32 + col, 2 * ds + half)));
 }
 
 // A-fragment of V^T for output dim tile dt and key step (kt, s): lane l holds
@@ -141,6 +158,83 @@ __device__ __forceinline__ bf16x8 v_frag(const char* vbase, int dt, int kt, int 
   v8i16 ab = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
   return __builtin_bit_cast(bf16x8, ab);
 }
+
+// 32-bit LDS address of a __shared__ object.
+__device__ __forceinline__ int lds_address(const void* p) {
+  return static_cast<int>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char*)p));
+}
+
+// x + c computed into a register whose value the compiler does not track,
+// at this point of the program (volatile: never hoisted out of a loop).
+__device__ __forceinline__ int opaque_add(int x, int c) {
+  int r;
+  asm volatile("v_add_u32 %0, %1, %2" : "=v"(r) : "s"(c), "v"(x));
+  return r;
+}
+
+// Fragment reads of one K or V region (the layouts above).  The swizzles
+// depend only on lane bits, so
+//  * the K A-fragment of sub-tile kt, head-dim step ds sits at
+//    k_off(col, 2ds + half) + kt*32*256;
+//  * the two transposed V reads of dim tile dt at key step (kt, s) sit at
+//    v_rel(4h + k, c) + (j&1)*8 + (32kt + 16s)*256 and the same at row
+//    4h + k + 8 (rows of the step; c = 4dt + 2(g&1) + j/2).
+// The constructor turns the per-lane parts into absolute LDS addresses held
+// in registers the compiler treats as opaque (computed where the object is
+// built, never hoisted); each read is then written as
+// region + (addr - region_address + imm), which the compiler reduces to
+// addr + imm: one register per offset and the immediate offset field,
+// whatever the region's place in LDS (LDS immediates are 16-bit, so a region
+// above 64 KiB would otherwise cost one address add per read).
+template <int BK>
+struct KReads {
+  const char* reg;
+  int ref;
+  int a[kDSteps];
+  __device__ __forceinline__ explicit KReads(const char* kreg) : reg(kreg), ref(lds_address(kreg)) {
+    const int lane = threadIdx.x & 63;
+    const int col = lane & 31;
+    const int half = lane >> 5;
+#pragma unroll
+    for (int ds = 0; ds < kDSteps; ++ds) a[ds] = opaque_add(TileLayout<BK>::k_off(col, 2 * ds + half), ref);
+  }
+  // K A-fragment of sub-tile kt, step ds
+  __device__ __forceinline__ bf16x8 frag(int kt, int ds) const {
+    return as_bf16x8(*reinterpret_cast<const u32x4*>(reg + (a[ds] - ref + kt * 32 * 256)));
+  }
+};
+
+template <int BK>
+struct VReads {
+  const char* reg;
+  int ref;
+  int a[kDTiles][2];
+  __device__ __forceinline__ explicit VReads(const char* vreg) : reg(vreg), ref(lds_address(vreg)) {
+    using L = TileLayout<BK>;
+    const int lane = threadIdx.x & 63;
+    const int i = lane & 15;
+    const int g = lane >> 4;
+    const int h = g >> 1;
+    const int kk = i >> 2;
+    const int j = i & 3;
+#pragma unroll
+    for (int dt = 0; dt < kDTiles; ++dt) {
+      const int c = dt * 4 + 2 * (g & 1) + (j >> 1);
+      a[dt][0] = opaque_add(L::v_rel(4 * h + kk, c) + (j & 1) * 8, ref);
+      a[dt][1] = opaque_add(L::v_rel(4 * h + kk + 8, c) + (j & 1) * 8, ref);
+    }
+  }
+  __device__ __forceinline__ bf16x8 frag(int dt, int kt, int s) const {
+    const int step = (32 * kt + 16 * s) * 256;
+    const char* p1 = reg + (a[dt][0] - ref + step);
+    const char* p2 = reg + (a[dt][1] - ref + step);
+    v4i16 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p1));
+    v4i16 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p2));
+    typedef short v8i16 __attribute__((ext_vector_type(8)));
+    v8i16 xy = __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8, xy);
+  }
+};
 
 __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 

@@ -142,12 +142,15 @@ rla_status rla_attn_prefill_chunked(const rla_attn_params* p, const void* q_chun
  * page_table[s][j / page_size] in the pools.
  * q [batch][Hq][128]; k_pool, v_pool [num_pages][Hkv][page_size][128] bf16;
  * page_table [batch][max_pages_per_seq] int32 (device); context_lens [batch]
- * int32 (device).  host_context_lens [host][batch] may be NULL; when given the
- * lengths are validated against max_context_len and the table width.
- * page_size must divide kv_block_size.  Lengths above
+ * int32 (device).  The kernels read the lengths from context_lens;
+ * host_context_lens [host][batch] may be NULL.  When given, the lengths are
+ * validated against max_context_len and the table width before anything is
+ * enqueued and the launch covers exactly the blocks they need; without it the
+ * launch covers every block up to max_context_len and idle workgroups exit
+ * (the results are the same bits either way).  page_size must divide kv_block_size.  Lengths above
  * min(max_context_len, max_pages_per_seq*page_size) are clamped to it, and a
- * page id outside [0, num_pages) is never dereferenced (its keys read as zero),
- * so a bad table cannot fault, but its result is unspecified.
+ * page id outside [0, num_pages) is clamped into that range before use, so a
+ * bad table cannot fault, but its result is unspecified.
  * workspace: at least rla_decode_workspace_bytes(p, batch, max_context_len)
  * bytes of device memory (per-block partial states); contents on return are
  * unspecified.  out [batch][Hq][128], lse [batch][Hq]. */

@@ -3,6 +3,8 @@ batch composition (a sequence alone vs in the batch) and to page placement
 (pages relocated in the pool).  Also: decode equals the last row of a prefill
 over the same tokens, bit for bit, because both run the same per-block core.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -92,6 +94,23 @@ def test_decode_equals_prefill_last_row():
         po, pl = api.prefill(dev_bf16(q), dev_bf16(k), dev_bf16(v), block=128, out_dtype=torch.float32)
         assert_bitwise(do[s], po[0, L - 1], f"seq {s} Out")
         assert_bitwise(dl[s], pl[0, L - 1], f"seq {s} LSE")
+
+
+@pytest.mark.parametrize("block,pages", [(128, (1, 2, 4, 8, 32, 64, 128)), (64, (1, 8, 32, 64))])
+def test_page_sizes_bitwise(block, pages):
+    """The page size only changes where keys live: every page size that
+    divides the block gives the bits of page size 16 (1 = one key per page,
+    where a block spans 128 pages; = block, one page per block)."""
+    d16 = gen.decode_inputs(SMALL, lengths=SMALL_LENS)
+    ref_o, ref_l = _decode(d16, SMALL, block=block, out_dtype=torch.float32)
+    for P in pages:
+        need = int((-(-SMALL_LENS.astype(np.int64) // P)).sum())
+        cfg = dataclasses.replace(SMALL, page_size=P, num_pages=need + 8)
+        say(f"[decode] page size {P} block={block}")
+        d = gen.decode_inputs(cfg, lengths=SMALL_LENS)
+        o, l = _decode(d, cfg, block=block, out_dtype=torch.float32)
+        assert_bitwise(o, ref_o, f"page size {P} Out")
+        assert_bitwise(l, ref_l, f"page size {P} LSE")
 
 
 def test_empty_context():

@@ -14,18 +14,17 @@
 //   softmax  mask, max, p, sum, bf16 P        (vector ALU)
 //   pv       acc_b = V^T P^T per dim tile     (matrix cores, V from LDS)
 //   fold     O_b = acc_b / l_b into the running state (vector ALU)
-// with the operations of core.hpp.  In fused mode the waves 0-3 (one per
-// SIMD) run the phases in that order and waves 4-7 run them one phase
-// later, with a workgroup barrier between phases: while one wave of a SIMD
-// is in a matrix-core phase the other is in a vector phase, so the two
-// units work at the same time.  LDS holds two blocks (double buffer); the
-// loads of block b+1 are issued when block b starts and waited for before
-// the last barrier of block b.  The per-block step takes the buffer being
-// read and the buffer being filled as restrict pointers, so the compiler
-// knows they do not overlap and never stalls an LDS read on the in-flight
-// loads (it would otherwise wait for every outstanding direct load before
-// the first read).  No atomics and no split of a block across workgroups,
-// so nothing depends on scheduling.
+// with the operations of core.hpp.  The bf16-output kernel is software
+// pipelined over blocks (prefill_pipe_kernel): a scores stage for block j,
+// then a vector stage that runs the softmax of block j slot by slot with the
+// PV MFMAs and the fold of block j-1, each stage ended by a workgroup
+// barrier.  The fp32-output kernel runs scores | softmax | pv+fold one after
+// the other.  K/V blocks arrive by direct buffer->LDS loads; the per-block
+// step takes the buffer being read and the buffer being filled as restrict
+// pointers, so the compiler knows they do not overlap and never stalls an
+// LDS read on the in-flight loads (it would otherwise wait for every
+// outstanding direct load before the first read).  No atomics and no split
+// of a block across workgroups, so nothing depends on scheduling.
 #include "kernels.hpp"
 #include "tile.hpp"
 

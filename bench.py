@@ -109,6 +109,58 @@ def cpu_baseline(q, k, v, cfg, seconds):
                       f"({flops(rows):.3e} flop, {dt:.1f} s, FP64)"}
 
 
+def reported_legs(api, up, stream):
+    """Reported (not the headline value): the long-context prefill (B=1,
+    S=32768, Q and K drawn x4) and the chunked-prefill replay of 8192 tokens
+    in chunks of 2048, 512 and 1.  TFLOP/s from the algorithmic flops of a
+    whole prefill / replay over the wall time of the launches (events on the
+    launch stream)."""
+    import torch
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    res = {}
+    cfg5 = gen.CFG5
+    log("long-context prefill (S=32768)")
+    q, k, v = gen.prefill_inputs(cfg5)
+    qd, kd, vd = up(q), up(k), up(v)
+    del q, k, v
+    ms = timed(lambda: api.prefill(qd, kd, vd, block=cfg5.block), 3)
+    res["long_prefill_b1_s32768"] = {"tflops": round(cfg5.flops() / (ms * 1e-3) / 1e12, 2), "ms": round(ms, 4),
+                                     "frac_of_peak": round(cfg5.flops() / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    del qd, kd, vd
+    torch.cuda.empty_cache()
+    cfg3 = gen.CFG3
+    q, k, v = gen.prefill_inputs(cfg3)
+    qd, kd, vd = up(q), up(k), up(v)
+    del q, k, v
+    for chunk in (2048, 512, 1):
+        log(f"chunked replay, chunk {chunk}")
+        parts = [(qd[:, c0:c0 + chunk].contiguous(), c0) for c0 in range(0, cfg3.S, chunk)]
+
+        def replay():
+            for qc, c0 in parts:
+                api.prefill_chunked(qc, kd, vd, cache_len=c0, block=cfg3.block)
+
+        ms = timed(replay, 1 if chunk == 1 else 3)
+        res[f"chunked_replay_s8192_c{chunk}"] = {"tflops": round(cfg3.flops() / (ms * 1e-3) / 1e12, 2),
+                                                 "ms": round(ms, 4), "calls": len(parts)}
+        del parts
+    del qd, kd, vd
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -117,6 +169,7 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=10)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-reported", action="store_true", help="skip the long-context and chunked-replay legs")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--only", choices=["prefill", "decode", "copy"], default=None,
                     help="run one leg only (for profiler and counter runs)")
@@ -211,6 +264,7 @@ def main():
     if args.only == "decode":
         print(json.dumps({"only": "decode", "decode": decode}))
         return
+    reported = None if args.no_reported else reported_legs(api, up, stream)
 
     line = {
         "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -224,6 +278,7 @@ def main():
                      "kernel_ms": round(kern_ms, 4)},
         "decode": decode,
         "invariance": {"batch_alone_vs_batch": drift_batch, "cp2_reversed_arrival": drift_cp},
+        "reported": reported,
         "cpu_baseline": base,
     }
     print(json.dumps(line), flush=True)

@@ -17,7 +17,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
-constexpr int kBatch = 8;  // items in flight per wave
+constexpr int kBatch = 32;  // items in flight per wave
 
 template <bool DECODE, bool F32>
 __global__ __launch_bounds__(kThreads) void fold_kernel(const FoldArgs a) {

@@ -19,8 +19,8 @@ RLA_ORDER_GLOBAL_BLOCK_INDEX, RLA_ORDER_ARRIVAL = 0, 1
 RLA_MAX_PARTS = 512
 
 # Every function include/rla_attn.h declares.
-EXPORTS = ("rla_attn_prefill", "rla_attn_prefill_chunked", "rla_attn_decode_paged", "rla_merge_states",
-           "rla_decode_workspace_bytes", "rla_last_error", "rla_core_id")
+EXPORTS = ("rla_attn_prefill", "rla_attn_prefill_chunked", "rla_attn_prefill_paged", "rla_attn_decode_paged",
+           "rla_merge_states", "rla_decode_workspace_bytes", "rla_last_error", "rla_core_id")
 
 
 class RlaParams(ctypes.Structure):
@@ -67,6 +67,8 @@ def load(path: str = LIB_PATH):
     lib.rla_attn_prefill.restype = ctypes.c_int
     lib.rla_attn_prefill_chunked.argtypes = [pp, P, P, P, i32, i32, i32, i32, ctypes.POINTER(RlaShard), P, P, P]
     lib.rla_attn_prefill_chunked.restype = ctypes.c_int
+    lib.rla_attn_prefill_paged.argtypes = [pp, P, P, P, i64, i32, P, i32, i32, i32, i32, P, P, P]
+    lib.rla_attn_prefill_paged.restype = ctypes.c_int
     lib.rla_attn_decode_paged.argtypes = [pp, P, P, P, i64, i32, P, i32, P, ctypes.POINTER(ctypes.c_int32),
                                           i32, i32, P, sz, P, P, P]
     lib.rla_attn_decode_paged.restype = ctypes.c_int

@@ -104,6 +104,24 @@ def prefill_chunked(q_chunk, k_cache, v_cache, *, cache_len, block, out_dtype=to
     return out, lse
 
 
+def prefill_paged(q_chunk, k_pool, v_pool, page_table, *, cache_len, block, out_dtype=torch.bfloat16, causal=True,
+                  scale=None):
+    """Chunked prefill over paged pools.  q_chunk [B,C,Hq,128]; pools
+    [num_pages,Hkv,P,128] bf16 already holding the chunk's K/V; page_table
+    [B,max_pages] int32 -> (out, lse)."""
+    B, C, Hq, D = q_chunk.shape
+    num_pages, Hkv, P, _ = k_pool.shape
+    p = params(Hq, Hkv, block=block, out_dtype=out_dtype, causal=causal, scale=scale, head_dim=D)
+    out = torch.empty((B, C, Hq, D), dtype=out_dtype, device=q_chunk.device)
+    lse = torch.empty((B, C, Hq), dtype=torch.float32, device=q_chunk.device)
+    lib = _lib.load()
+    _lib.check(lib.rla_attn_prefill_paged(
+        ctypes.byref(p), _dev(q_chunk, "q_chunk", torch.bfloat16, 4), _dev(k_pool, "k_pool", torch.bfloat16, 4),
+        _dev(v_pool, "v_pool", torch.bfloat16, 4), num_pages, P, _dev(page_table, "page_table", torch.int32, 2),
+        page_table.shape[1], B, C, int(cache_len), out.data_ptr(), lse.data_ptr(), _stream(q_chunk.device)))
+    return out, lse
+
+
 def emit_partials(q, k, v, kv_blocks, *, block, out_dtype=torch.bfloat16, causal=True, scale=None, q_begin=0,
                   q_count=None, cache_len=None, part_out=None, part_lse=None):
     """Per-block partial states of the owned ``kv_blocks`` (emulated CP shard).

@@ -170,6 +170,58 @@ rla_status rla_attn_prefill_chunked(const rla_attn_params* p, const void* q_chun
                         static_cast<int64_t>(cache_len) + chunk_len, s_max, shard, out, lse, hip_stream);
 }
 
+rla_status rla_attn_prefill_paged(const rla_attn_params* p, const void* q_chunk, const void* k_pool,
+                                  const void* v_pool, int64_t num_pages, int32_t page_size,
+                                  const int32_t* page_table, int32_t max_pages_per_seq, int32_t batch,
+                                  int32_t chunk_len, int32_t cache_len, void* out, float* lse,
+                                  void* hip_stream) {
+  int g = 0;
+  rla_status st = check_params(p, true, &g);
+  if (st != RLA_OK) return st;
+  if (q_chunk == nullptr || k_pool == nullptr || v_pool == nullptr || page_table == nullptr || out == nullptr ||
+      lse == nullptr)
+    return fail(RLA_ERR_NULL_POINTER, "a required pointer is NULL");
+  if (batch < 1 || chunk_len < 1 || cache_len < 0 || num_pages < 1 || max_pages_per_seq < 1)
+    return fail(RLA_ERR_BAD_SHAPE, "need batch>=1, chunk_len>=1, cache_len>=0, num_pages>=1, max_pages_per_seq>=1");
+  if (num_pages > 0x7fffffff) return fail(RLA_ERR_BAD_SHAPE, "num_pages exceeds int32 page ids");
+  if (page_size < 4 || page_size > p->kv_block_size || (page_size & (page_size - 1)) != 0)
+    return fail(RLA_ERR_UNSUPPORTED, "page_size=%d must be a power of two in [4, kv_block_size=%d]", page_size,
+                p->kv_block_size);
+  const int64_t kv_len = static_cast<int64_t>(cache_len) + chunk_len;
+  if (static_cast<int64_t>(max_pages_per_seq) * page_size < kv_len)
+    return fail(RLA_ERR_BAD_SHAPE, "max_pages_per_seq*page_size=%lld does not cover cache_len+chunk_len=%lld",
+                (long long)max_pages_per_seq * page_size, (long long)kv_len);
+  if (kv_len > 0x7fffffff) return fail(RLA_ERR_BAD_SHAPE, "cache_len+chunk_len exceeds int32 positions");
+  const int Hq = p->num_q_heads, D = rla::kHeadDimPublic;
+
+  rla::PrefillArgs a;
+  std::memset(&a, 0, sizeof a);
+  a.q = static_cast<const uint16_t*>(q_chunk);
+  a.k = static_cast<const uint16_t*>(k_pool);
+  a.v = static_cast<const uint16_t*>(v_pool);
+  a.q_bstride = static_cast<int64_t>(chunk_len) * Hq * D;
+  a.kv_bstride = 0;  // keys come through the page table
+  a.pos0 = cache_len;
+  a.kv_len = kv_len;
+  a.B = batch;
+  a.Sq = chunk_len;
+  a.Hq = Hq;
+  a.Hkv = p->num_kv_heads;
+  a.G = g;
+  a.causal = p->causal;
+  a.c = score_scale(p);
+  a.out = out;
+  a.lse = lse;
+  a.page_table = page_table;
+  a.num_pages = num_pages;
+  a.max_pages = max_pages_per_seq;
+  a.log2_P = 0;
+  while ((1 << a.log2_P) < page_size) ++a.log2_P;
+  hipError_t e = rla::launch_prefill_paged(a, p->kv_block_size, p->out_dtype == RLA_DT_FP32,
+                                           static_cast<hipStream_t>(hip_stream));
+  return hip_status(e, "paged prefill launch");
+}
+
 size_t rla_decode_workspace_bytes(const rla_attn_params* p, int32_t batch, int32_t max_context_len) {
   int g = 0;
   if (check_params(p, true, &g) != RLA_OK || batch < 1 || max_context_len < 0) return 0;

@@ -35,6 +35,10 @@ struct PrefillArgs {
   int32_t n_ptiles;          // position tiles of 32*pos_groups rows
   int32_t causal;
   float c;                   // softmax_scale * log2(e), rounded to fp32
+  const int32_t* page_table; // paged mode: [B][max_pages] page ids; k and v are the pools
+  int64_t num_pages;         // paged mode: pages in each pool [num_pages][Hkv][P][D]
+  int32_t log2_P;            // paged mode: log2 of the page size (P >= 4)
+  int32_t max_pages;         // paged mode: table row length
   int32_t n_emit;            // emit mode: number of owned blocks
   uint16_t emit_blocks[kMaxParts];
 };
@@ -78,6 +82,8 @@ struct FoldArgs {
 };
 
 hipError_t launch_prefill(const PrefillArgs& a, int block, bool out_f32, bool emit, hipStream_t s);
+// Fused prefill with K/V gathered from paged pools (a.page_table etc. set).
+hipError_t launch_prefill_paged(const PrefillArgs& a, int block, bool out_f32, hipStream_t s);
 hipError_t launch_decode_items(const DecodeArgs& a, int block, bool out_f32, hipStream_t s);
 hipError_t launch_fold(const FoldArgs& a, bool decode, bool out_f32, hipStream_t s);
 

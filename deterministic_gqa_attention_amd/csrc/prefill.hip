@@ -418,7 +418,7 @@ __device__ __forceinline__ void write_out(const PrefillArgs& a, const TileMap& t
 // stage of iteration j) and must land by the end of that iteration.  The
 // step takes the regions as restrict pointers, so the compiler does not
 // stall LDS reads of one region on the in-flight loads into another.
-template <int BK>
+template <int BK, bool PAGED>
 __global__ __launch_bounds__(kThreads) void prefill_pipe_kernel(const PrefillArgs a) {
   using L = TileLayout<BK>;
   using Ld = BlockLoader<BK, kWaves>;
@@ -440,6 +440,23 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe_kernel(const PrefillArg
 
   Ld ld;
   ld.init(static_cast<int>(w.row_stride));
+  PagedLoader<BK, kWaves> pl;
+  if constexpr (PAGED)
+    pl.init(a.page_table + static_cast<int64_t>(tm.b) * a.max_pages, a.log2_P, a.kv_len, a.num_pages, a.Hkv, tm.hk);
+  auto issue_k = [&](char* dst, int64_t key0) {
+    if constexpr (PAGED) {
+      pl.template issue<false>(dst, a.k, key0);
+    } else {
+      ld.issue_k(dst, w.krs, key0);
+    }
+  };
+  auto issue_v = [&](char* dst, int64_t key0) {
+    if constexpr (PAGED) {
+      pl.template issue<true>(dst, a.v, key0);
+    } else {
+      ld.issue_v(dst, w.vrs, key0);
+    }
+  };
   // this lane's Q fragments, step ds at qlane + ds*1024
   char* const qlane = qbuf + ld.wave * (32 * kHeadDim * 2) + (threadIdx.x & 63) * 16;
 #pragma unroll
@@ -447,7 +464,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe_kernel(const PrefillArg
   // V buffer 1 stands for block -1 in the first step: zeros
   for (int i = threadIdx.x; i < L::kVBytes / 16; i += kThreads)
     *reinterpret_cast<u32x4*>(vbuf + L::kVBytes + 16 * i) = u32x4{0, 0, 0, 0};
-  if (nblk > 0) ld.issue_k(kbuf, w.krs, 0);
+  if (nblk > 0) issue_k(kbuf, 0);
   wait_direct_loads();  // K_0
   lds_barrier();
 
@@ -460,7 +477,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe_kernel(const PrefillArg
   // of block j-1 (pending pv+fold when pend).
   auto step = [&](int64_t blk, char* __restrict__ kc, char* __restrict__ vn, const char* __restrict__ vp, P& Pn,
                   FoldIn& inn, const P& Pp, const FoldIn& inp, bool& pend) {
-    if (blk < nblk) ld.issue_v(vn, w.vrs, blk * BK);
+    if (blk < nblk) issue_v(vn, blk * BK);
     const bool sm = blk < nblk && wave_sees<BK>(a, tm, blk);
     f32x16 s[BK / 32];
     if (sm) block_scores_q<BK>(kc, qlane, s);
@@ -468,7 +485,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe_kernel(const PrefillArg
     sched_fence();
     wait_loads_leq<Ld::NI>(cnt(blk));  // V_{j-1} landed (V_j may be in flight)
     lds_barrier();
-    if (blk + 1 < nblk) ld.issue_k(kc, w.krs, (blk + 1) * BK);
+    if (blk + 1 < nblk) issue_k(kc, (blk + 1) * BK);
     if (sm && !wave_full<BK>(a, tm, blk)) apply_mask<BK>(s, static_cast<int>(blk * BK), kvl, a.causal, qpos);
     if (pend && inp.any_move) {
 #pragma unroll
@@ -500,6 +517,9 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe_kernel(const PrefillArg
     pend = sm;
     sched_fence();
     wait_direct_loads();  // K_{j+1} (and V_j) landed
+    if constexpr (PAGED) {
+      if (blk < nblk && (blk + 1) * BK > a.kv_len) pl.clear_tail(vn, blk * BK, a.kv_len);
+    }
     lds_barrier();
   };
 
@@ -522,7 +542,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe_kernel(const PrefillArg
 // into the K buffer of block j in the third phase of block j and V_{j+1}
 // into the other V buffer in the second phase, so each load has about four
 // phases to land.
-template <int BK, bool F32>
+template <int BK, bool F32, bool PAGED>
 __global__ __launch_bounds__(kThreads) void prefill_fused_kernel(const PrefillArgs a) {
   using L = TileLayout<BK>;
   using Ld = BlockLoader<BK, kWaves>;
@@ -543,12 +563,29 @@ __global__ __launch_bounds__(kThreads) void prefill_fused_kernel(const PrefillAr
   sched_fence();  // the Q loads of wave_setup stay ahead of the direct loads
   Ld ld;
   ld.init(static_cast<int>(w.row_stride));
+  PagedLoader<BK, kWaves> pl;
+  if constexpr (PAGED)
+    pl.init(a.page_table + static_cast<int64_t>(tm.b) * a.max_pages, a.log2_P, a.kv_len, a.num_pages, a.Hkv, tm.hk);
+  auto issue_k = [&](char* dst, int64_t key0) {
+    if constexpr (PAGED) {
+      pl.template issue<false>(dst, a.k, key0);
+    } else {
+      ld.issue_k(dst, w.krs, key0);
+    }
+  };
+  auto issue_v = [&](char* dst, int64_t key0) {
+    if constexpr (PAGED) {
+      pl.template issue<true>(dst, a.v, key0);
+    } else {
+      ld.issue_v(dst, w.vrs, key0);
+    }
+  };
   auto cnt = [&](int64_t blk) { return blk < nblk ? Ld::NI : 0; };  // loads of one region of blk
   if (nblk > 0) {
-    ld.issue_k(kbuf, w.krs, 0);
-    ld.issue_v(vbuf, w.vrs, 0);
+    issue_k(kbuf, 0);
+    issue_v(vbuf, 0);
   }
-  if (nblk > 1) ld.issue_k(kbuf + L::kKBytes, w.krs, BK);
+  if (nblk > 1) issue_k(kbuf + L::kKBytes, BK);
   wait_direct_loads();  // Q, K_0, V_0, K_1
   lds_barrier();
 
@@ -564,7 +601,7 @@ __global__ __launch_bounds__(kThreads) void prefill_fused_kernel(const PrefillAr
     if (sees) block_scores<BK>(kc, w.qf, s);
     sched_fence();
     lds_barrier();
-    if (blk + 1 < nblk) ld.issue_v(vn, w.vrs, (blk + 1) * BK);
+    if (blk + 1 < nblk) issue_v(vn, (blk + 1) * BK);
     FoldIn in{};
     if (sees) {
       block_softmax<BK, F32>(s, !wave_full<BK>(a, tm, blk), static_cast<int>(blk * BK), kvl, a.causal, qpos, a.c, P);
@@ -572,8 +609,11 @@ __global__ __launch_bounds__(kThreads) void prefill_fused_kernel(const PrefillAr
     }
     sched_fence();
     wait_loads_leq<Ld::NI>(cnt(blk + 1) + cnt(blk + 1));  // V of blk landed
+    if constexpr (PAGED) {
+      if ((blk + 1) * BK > a.kv_len) pl.clear_tail(const_cast<char*>(vc), blk * BK, a.kv_len);
+    }
     lds_barrier();
-    if (blk + 2 < nblk) ld.issue_k(kc, w.krs, (blk + 2) * BK);
+    if (blk + 2 < nblk) issue_k(kc, (blk + 2) * BK);
     if (sees) block_pv_fold<BK, F32>(VReads<BK>(vc), P, in, acc);
     sched_fence();
     wait_loads_leq<Ld::NI>(cnt(blk + 1) + cnt(blk + 2));  // K of blk+1 landed
@@ -650,7 +690,7 @@ __global__ __launch_bounds__(kThreads) void prefill_emit_kernel(const PrefillArg
   if (half == 0) a.part_lse[prow * a.Hq + tm.head] = sc.L;
 }
 
-template <int BK, bool F32, bool EMIT>
+template <int BK, bool F32, bool EMIT, bool PAGED = false>
 hipError_t launch_t(PrefillArgs a, hipStream_t s) {
   // tile = up to 8 column tiles of 32 positions: heads of the group first
   // (the largest divisor of G that fits), then positions
@@ -668,9 +708,10 @@ hipError_t launch_t(PrefillArgs a, hipStream_t s) {
   if constexpr (EMIT) {
     hipLaunchKernelGGL((prefill_emit_kernel<BK, F32>), dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, s, a);
   } else if constexpr (F32) {
-    hipLaunchKernelGGL((prefill_fused_kernel<BK, F32>), dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((prefill_fused_kernel<BK, F32, PAGED>), dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, s,
+                       a);
   } else {
-    hipLaunchKernelGGL((prefill_pipe_kernel<BK>), dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((prefill_pipe_kernel<BK, PAGED>), dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, s, a);
   }
   return hipGetLastError();
 }
@@ -686,6 +727,13 @@ hipError_t launch_prefill(const PrefillArgs& a, int block, bool out_f32, bool em
     if (out_f32) return emit ? launch_t<64, true, true>(a, s) : launch_t<64, true, false>(a, s);
     return emit ? launch_t<64, false, true>(a, s) : launch_t<64, false, false>(a, s);
   }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_prefill_paged(const PrefillArgs& a, int block, bool out_f32, hipStream_t s) {
+  if (a.page_table == nullptr || a.log2_P < 2 || (1 << a.log2_P) > block) return hipErrorInvalidValue;
+  if (block == 128) return out_f32 ? launch_t<128, true, false, true>(a, s) : launch_t<128, false, false, true>(a, s);
+  if (block == 64) return out_f32 ? launch_t<64, true, false, true>(a, s) : launch_t<64, false, false, true>(a, s);
   return hipErrorInvalidValue;
 }
 

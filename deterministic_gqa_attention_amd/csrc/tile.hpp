@@ -107,6 +107,74 @@ struct BlockLoader {
   }
 };
 
+// Direct global->LDS loads of one KV block gathered through a page table:
+// the pool is [page][kv head][slot][128] with page size P >= 4, so the 4
+// consecutive keys of one load instruction lie in one page.  That page,
+// read from the table by a scalar load, is uniform across the wave; the lanes
+// only add their row within the group and their swizzled chunk, and the LDS
+// side is the layout of BlockLoader.  Keys at or past kv_len read the
+// sequence's last page (clear_tail then zeroes their V rows in LDS); page ids
+// outside [0, num_pages) are clamped into the pool, so a bad table cannot
+// fault (its result is unspecified).
+template <int BK, int NW>
+struct PagedLoader {
+  using L = TileLayout<BK>;
+  static constexpr int NI = L::kLoadsPerRegion / NW;
+  static_assert(NW % 4 == 0, "swizzle bits must not depend on the load index");
+  int wave;
+  int kbyte0;               // lane's byte offset within its 4-row group (K swizzle)
+  int vbyte0;               // the same with the V swizzle
+  const int32_t* table;     // page ids of this sequence
+  int log2_P;
+  int last_idx;             // table index of the page that holds key kv_len-1
+  int64_t num_pages;
+  int64_t page_elems;       // Hkv * P * 128
+  int64_t head_elems;       // hk * P * 128
+
+  __device__ __forceinline__ void init(const int32_t* tab, int lp, int64_t kv_len, int64_t pages, int Hkv, int hk) {
+    wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+    const int lane = threadIdx.x & 63;
+    const int g = lane >> 4;
+    const int p = lane & 15;
+    const int r = 4 * wave + g;
+    kbyte0 = g * 256 + ((p ^ L::k_swz(r)) << 4);
+    vbyte0 = g * 256 + ((p ^ L::v_swz(r)) << 4);
+    table = tab;
+    log2_P = lp;
+    last_idx = kv_len > 0 ? static_cast<int>((kv_len - 1) >> lp) : 0;
+    num_pages = pages;
+    page_elems = static_cast<int64_t>(Hkv) * (int64_t{1} << lp) * kHeadDim;
+    head_elems = static_cast<int64_t>(hk) * (int64_t{1} << lp) * kHeadDim;
+  }
+
+  template <bool V>
+  __device__ __forceinline__ void issue(char* dst, const uint16_t* pool, int64_t key0) const {
+    typedef const __attribute__((address_space(4))) int32_t ctab;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int n = wave + NW * i;
+      const int64_t key = key0 + 4 * n;
+      const int idx = min(static_cast<int>(key >> log2_P), last_idx);
+      int64_t page = ((ctab*)table)[idx];
+      page = page < 0 ? 0 : (page >= num_pages ? num_pages - 1 : page);
+      const int64_t slot = key & ((int64_t{1} << log2_P) - 1);
+      const char* base = reinterpret_cast<const char*>(pool + page * page_elems + head_elems + slot * kHeadDim);
+      direct_load16(reinterpret_cast<const uint16_t*>(base + (V ? vbyte0 : kbyte0)), dst + n * 1024);
+    }
+  }
+
+  // Zero the rows at or past kv_len among those this wave loaded for the
+  // block at key0 (call once the loads have landed).
+  __device__ __forceinline__ void clear_tail(char* dst, int64_t key0, int64_t kv_len) const {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int n = wave + NW * i;
+      if (key0 + 4 * n + (lane >> 4) >= kv_len) *reinterpret_cast<u32x4*>(dst + n * 1024 + lane * 16) = u32x4{0, 0, 0, 0};
+    }
+  }
+};
+
 // Wait until at most n of this wave's vector-memory loads are outstanding
 // (they retire in issue order); n is one of 0, NI, 2*NI of a loader, chosen
 // by a wave-uniform branch so the count stays an immediate.

@@ -136,6 +136,28 @@ rla_status rla_attn_prefill_chunked(const rla_attn_params* p, const void* q_chun
                                     int32_t cache_len, int32_t s_max, const rla_shard* shard, void* out,
                                     float* lse, void* hip_stream);
 
+/* Paged chunked prefill ("Commands": paged prefill/decode with batch and
+ * page-layout invariance): rla_attn_prefill_chunked with the keys gathered
+ * through a page table instead of read from a contiguous cache.  Query i of
+ * the chunk sits at position cache_len + i and attends keys [0, cache_len + i]
+ * (causal; all cache_len + chunk_len keys when p->causal == 0); key j of
+ * sequence b is slot j % page_size of page page_table[b][j / page_size].
+ * q_chunk [batch][chunk_len][Hq][128] bf16; k_pool, v_pool
+ * [num_pages][Hkv][page_size][128] bf16 already holding the chunk's keys;
+ * page_table [batch][max_pages_per_seq] int32 (device).  page_size must be a
+ * power of two with 4 <= page_size <= kv_block_size (one load instruction
+ * covers 4 consecutive keys of one page), and max_pages_per_seq * page_size
+ * must cover cache_len + chunk_len.  A page id outside [0, num_pages) is
+ * clamped into that range before use, so a bad table cannot fault, but its
+ * result is unspecified.  The result is bit for bit that of
+ * rla_attn_prefill_chunked over the same keys, whatever the page layout.
+ * out [batch][chunk_len][Hq][128] (bf16 or fp32), lse [batch][chunk_len][Hq]. */
+rla_status rla_attn_prefill_paged(const rla_attn_params* p, const void* q_chunk, const void* k_pool,
+                                  const void* v_pool, int64_t num_pages, int32_t page_size,
+                                  const int32_t* page_table, int32_t max_pages_per_seq, int32_t batch,
+                                  int32_t chunk_len, int32_t cache_len, void* out, float* lse,
+                                  void* hip_stream);
+
 /* Paged-KV decode ("Commands": paged prefill/decode with batch and page-layout
  * invariance): one query token per sequence attending its cached keys
  * [0, context_lens[s]).  Key j of sequence s is slot j % page_size of page
@@ -147,7 +169,8 @@ rla_status rla_attn_prefill_chunked(const rla_attn_params* p, const void* q_chun
  * validated against max_context_len and the table width before anything is
  * enqueued and the launch covers exactly the blocks they need; without it the
  * launch covers every block up to max_context_len and idle workgroups exit
- * (the results are the same bits either way).  page_size must divide kv_block_size.  Lengths above
+ * (the results are the same bits either way).  page_size must divide
+ * kv_block_size.  Lengths above
  * min(max_context_len, max_pages_per_seq*page_size) are clamped to it, and a
  * page id outside [0, num_pages) is clamped into that range before use, so a
  * bad table cannot fault, but its result is unspecified.

@@ -85,6 +85,21 @@ def test_chunked_rejects_overflowing_cache(lib):
     assert st == 2
 
 
+def test_paged_prefill_rejects_bad_args(lib):
+    p = _params()
+    # (num_pages, page_size, max_pages, batch, chunk, cache) -> status
+    call = lambda np_, ps, mp, b, c, cl, q=FAKE: lib.rla_attn_prefill_paged(
+        ctypes.byref(p), q, FAKE, FAKE, np_, ps, FAKE, mp, b, c, cl, FAKE, FAKE, None)
+    assert call(64, 16, 8, 1, 16, 0, q=None) == 1            # NULL q
+    assert call(64, 2, 64, 1, 16, 0) == 3                    # page size below 4
+    assert call(64, 24, 8, 1, 16, 0) == 3                    # not a power of two
+    assert call(64, 256, 1, 1, 16, 0) == 3                   # larger than the block
+    assert call(64, 16, 4, 1, 16, 60) == 2                   # table covers 64 keys, chunk ends at 76
+    assert "max_pages_per_seq" in lib.rla_last_error().decode()
+    assert call(64, 16, 8, 1, 0, 0) == 2                     # empty chunk
+    assert call(0, 16, 8, 1, 16, 0) == 2                     # empty pool
+
+
 def _shard(blocks, q_begin=0, q_count=16, n_parts=None, rows=16):
     arr = (ctypes.c_int64 * len(blocks))(*blocks)
     parts = _lib.RlaPartials(out=FAKE.value, lse=FAKE.value, global_block_index=arr,

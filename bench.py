@@ -156,7 +156,25 @@ def reported_legs(api, up, stream):
         res[f"chunked_replay_s8192_c{chunk}"] = {"tflops": round(cfg3.flops() / (ms * 1e-3) / 1e12, 2),
                                                  "ms": round(ms, 4), "calls": len(parts)}
         del parts
-    del qd, kd, vd
+    # the same replay (chunks of 2048) with the keys in a paged pool of 16-key pages
+    P = 16
+    npp = cfg3.S // P
+    perm = np.random.Generator(np.random.PCG64(1000 * cfg3.cfg_id + 5)).permutation(npp)
+    table = torch.from_numpy(perm.astype(np.int32).reshape(1, npp)).to(qd.device)
+    inv = torch.from_numpy(np.argsort(perm)).to(qd.device)  # pool slot p holds logical page inv[p]
+    kp = kd[0].reshape(npp, P, cfg3.Hkv, cfg3.D).transpose(1, 2)[inv].contiguous()
+    vp = vd[0].reshape(npp, P, cfg3.Hkv, cfg3.D).transpose(1, 2)[inv].contiguous()
+    parts = [(qd[:, c0:c0 + 2048].contiguous(), c0) for c0 in range(0, cfg3.S, 2048)]
+
+    def paged_replay():
+        for qc, c0 in parts:
+            api.prefill_paged(qc, kp, vp, table, cache_len=c0, block=cfg3.block)
+
+    log("paged chunked replay, chunk 2048")
+    ms = timed(paged_replay, 3)
+    res["paged_replay_s8192_c2048_p16"] = {"tflops": round(cfg3.flops() / (ms * 1e-3) / 1e12, 2), "ms": round(ms, 4),
+                                            "calls": len(parts)}
+    del parts, kp, vp, qd, kd, vd
     torch.cuda.empty_cache()
     return res
 

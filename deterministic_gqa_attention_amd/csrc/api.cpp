@@ -8,6 +8,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "kernels.hpp"
@@ -16,6 +17,8 @@
 namespace {
 
 thread_local char g_err[512] = "";
+
+constexpr int kMaxDevices = 64;
 
 rla_status fail(rla_status st, const char* fmt, ...) {
   va_list ap;
@@ -142,6 +145,134 @@ rla_status prefill_common(const rla_attn_params* p, const void* q, const void* k
   return hip_status(e, "prefill launch");
 }
 
+// The two decode launches (block items, ordered fold) after validation.
+// context_lens == nullptr: every sequence has uniform_len keys; page_table ==
+// nullptr: page i of sequence s is s*max_pages_per_seq + i.
+rla_status run_decode(const rla_attn_params* p, int g, const void* q, const void* k_pool, const void* v_pool,
+                      int64_t num_pages, int32_t page_size, const int32_t* page_table, int32_t max_pages_per_seq,
+                      const int32_t* context_lens, int32_t uniform_len, const int32_t* host_context_lens,
+                      int32_t batch, int32_t max_context_len, int64_t cap, void* workspace, void* out, float* lse,
+                      hipStream_t s) {
+  const int64_t max_blocks = std::max<int64_t>(1, (static_cast<int64_t>(max_context_len) + p->kv_block_size - 1) /
+                                                      p->kv_block_size);
+  const int64_t items = static_cast<int64_t>(batch) * max_blocks * p->num_q_heads;
+  const int64_t out_bytes = (items * rla::kHeadDimPublic * 4 + 255) / 256 * 256;
+  float* items_out = static_cast<float*>(workspace);
+  float* items_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + out_bytes);
+
+  rla::DecodeArgs d;
+  std::memset(&d, 0, sizeof d);
+  d.q = static_cast<const uint16_t*>(q);
+  d.k_pool = static_cast<const uint16_t*>(k_pool);
+  d.v_pool = static_cast<const uint16_t*>(v_pool);
+  d.page_table = page_table;
+  d.ctx_lens = context_lens;
+  d.uniform_len = uniform_len;
+  d.items_out = items_out;
+  d.items_lse = items_lse;
+  d.num_pages = num_pages;
+  d.P = page_size;
+  d.log2_P = 0;
+  while ((1 << d.log2_P) < page_size) ++d.log2_P;  // page_size divides 64 or 128: a power of two
+  d.max_pages = max_pages_per_seq;
+  d.Bd = batch;
+  d.Hq = p->num_q_heads;
+  d.Hkv = p->num_kv_heads;
+  d.G = g;
+  d.max_blocks = static_cast<int32_t>(max_blocks);
+  d.len_cap = static_cast<int32_t>(cap);
+  d.c = score_scale(p);
+  d.unit_blocks = rla::kDecodeUnitBlocks;
+  if (host_context_lens != nullptr || context_lens == nullptr) {
+    // compact grid: exactly the units the lengths need
+    int64_t units = 0;
+    for (int i = 0; i < batch; ++i) {
+      const int64_t len = context_lens == nullptr ? uniform_len : host_context_lens[i];
+      const int64_t nb = (len + p->kv_block_size - 1) / p->kv_block_size;
+      units += (nb + rla::kDecodeUnitBlocks - 1) / rla::kDecodeUnitBlocks;
+    }
+    d.compact = 1;
+    d.n_units = units;
+  } else {
+    d.compact = 0;
+    d.n_units = static_cast<int64_t>(batch) * ((max_blocks + rla::kDecodeUnitBlocks - 1) / rla::kDecodeUnitBlocks);
+  }
+  const bool f32 = p->out_dtype == RLA_DT_FP32;
+  hipError_t e = rla::launch_decode_items(d, p->kv_block_size, f32, s);
+  if (e != hipSuccess) return hip_status(e, "decode launch");
+
+  rla::FoldArgs f;
+  std::memset(&f, 0, sizeof f);
+  f.part_out = items_out;
+  f.part_lse = items_lse;
+  f.ctx_lens = context_lens;
+  f.uniform_len = uniform_len;
+  f.out = out;
+  f.lse = lse;
+  f.rows = batch;
+  f.Hq = p->num_q_heads;
+  f.n_parts = static_cast<int32_t>(max_blocks);
+  f.block = p->kv_block_size;
+  f.len_cap = static_cast<int32_t>(cap);
+  e = rla::launch_fold(f, true, f32, s);
+  return hip_status(e, "decode fold launch");
+}
+
+// Device scratch for one call, stream-ordered, from a memory pool of the
+// library's own that keeps what is freed (release threshold: unlimited), so
+// calls after the first reuse the pool's memory instead of allocating.
+hipError_t scratch_alloc(void** ptr, size_t bytes, hipStream_t s) {
+  static std::mutex mu;
+  static hipMemPool_t pools[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    if (pools[dev] == nullptr) {
+      hipMemPoolProps props;
+      std::memset(&props, 0, sizeof props);
+      props.allocType = hipMemAllocationTypePinned;
+      props.location.type = hipMemLocationTypeDevice;
+      props.location.id = dev;
+      hipMemPool_t pool = nullptr;
+      e = hipMemPoolCreate(&pool, &props);
+      if (e != hipSuccess) return e;
+      uint64_t keep = UINT64_MAX;
+      e = hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep);
+      if (e != hipSuccess) return e;
+      pools[dev] = pool;
+    }
+  }
+  return hipMallocFromPoolAsync(ptr, bytes, pools[dev], s);
+}
+
+// A chunk of one query is a decode step over the cache: the contiguous cache
+// [B][s_max][Hkv][128] is a paged pool with one key per page (page id
+// b*s_max + j), so the decode kernels run it, spreading the KV blocks over
+// many workgroups and folding the block items in order.  Their per-(row,
+// block) arithmetic is that of the prefill kernels, so the bits are the same.
+// Returns false (nothing done) when the cache is too large for int32 page ids.
+bool single_query_chunk(const rla_attn_params* p, int g, const void* q, const void* k_cache, const void* v_cache,
+                        int32_t batch, int32_t cache_len, int32_t s_max, void* out, float* lse, hipStream_t s,
+                        rla_status* st) {
+  if (static_cast<int64_t>(batch) * s_max > 0x7fffffff) return false;
+  const int32_t len = cache_len + 1;
+  const size_t bytes = rla_decode_workspace_bytes(p, batch, len);
+  void* ws = nullptr;
+  hipError_t e = scratch_alloc(&ws, bytes, s);
+  if (e != hipSuccess) {
+    *st = hip_status(e, "chunk scratch");
+    return true;
+  }
+  *st = run_decode(p, g, q, k_cache, v_cache, static_cast<int64_t>(batch) * s_max, 1, nullptr, s_max, nullptr, len,
+                   nullptr, batch, len, len, ws, out, lse, s);
+  e = hipFreeAsync(ws, s);
+  if (*st == RLA_OK && e != hipSuccess) *st = hip_status(e, "chunk scratch free");
+  return true;
+}
+
 }  // namespace
 
 extern "C" {
@@ -166,6 +297,17 @@ rla_status rla_attn_prefill_chunked(const rla_attn_params* p, const void* q_chun
       static_cast<int64_t>(cache_len) + chunk_len > s_max)
     return fail(RLA_ERR_BAD_SHAPE, "need batch>=1, chunk_len>=1, cache_len>=0, cache_len+chunk_len<=s_max "
                 "(got %d, %d, %d, %d)", batch, chunk_len, cache_len, s_max);
+  if (chunk_len == 1 && shard == nullptr) {
+    int g = 0;
+    const rla_status st0 = check_params(p, true, &g);
+    if (st0 != RLA_OK) return st0;
+    if (q_chunk == nullptr || k_cache == nullptr || v_cache == nullptr || out == nullptr || lse == nullptr)
+      return fail(RLA_ERR_NULL_POINTER, "a required pointer is NULL");
+    rla_status st = RLA_OK;
+    if (single_query_chunk(p, g, q_chunk, k_cache, v_cache, batch, cache_len, s_max, out, lse,
+                           static_cast<hipStream_t>(hip_stream), &st))
+      return st;
+  }
   return prefill_common(p, q_chunk, k_cache, v_cache, batch, chunk_len, cache_len,
                         static_cast<int64_t>(cache_len) + chunk_len, s_max, shard, out, lse, hip_stream);
 }
@@ -260,67 +402,9 @@ rla_status rla_attn_decode_paged(const rla_attn_params* p, const void* q, const 
   const size_t need = rla_decode_workspace_bytes(p, batch, max_context_len);
   if (workspace_bytes < need)
     return fail(RLA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", workspace_bytes, need);
-  const int64_t max_blocks = std::max<int64_t>(1, (static_cast<int64_t>(max_context_len) + p->kv_block_size - 1) /
-                                                      p->kv_block_size);
-  const int64_t items = static_cast<int64_t>(batch) * max_blocks * p->num_q_heads;
-  const int64_t out_bytes = (items * rla::kHeadDimPublic * 4 + 255) / 256 * 256;
-  float* items_out = static_cast<float*>(workspace);
-  float* items_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + out_bytes);
-
-  rla::DecodeArgs d;
-  std::memset(&d, 0, sizeof d);
-  d.q = static_cast<const uint16_t*>(q);
-  d.k_pool = static_cast<const uint16_t*>(k_pool);
-  d.v_pool = static_cast<const uint16_t*>(v_pool);
-  d.page_table = page_table;
-  d.ctx_lens = context_lens;
-  d.items_out = items_out;
-  d.items_lse = items_lse;
-  d.num_pages = num_pages;
-  d.P = page_size;
-  d.log2_P = 0;
-  while ((1 << d.log2_P) < page_size) ++d.log2_P;  // page_size divides 64 or 128: a power of two
-  d.max_pages = max_pages_per_seq;
-  d.Bd = batch;
-  d.Hq = p->num_q_heads;
-  d.Hkv = p->num_kv_heads;
-  d.G = g;
-  d.max_blocks = static_cast<int32_t>(max_blocks);
-  d.len_cap = static_cast<int32_t>(cap);
-  d.c = score_scale(p);
-  d.unit_blocks = rla::kDecodeUnitBlocks;
-  if (host_context_lens != nullptr) {
-    // compact grid: exactly the units the lengths need
-    int64_t units = 0;
-    for (int i = 0; i < batch; ++i) {
-      const int64_t nb = (host_context_lens[i] + p->kv_block_size - 1) / p->kv_block_size;
-      units += (nb + rla::kDecodeUnitBlocks - 1) / rla::kDecodeUnitBlocks;
-    }
-    d.compact = 1;
-    d.n_units = units;
-  } else {
-    d.compact = 0;
-    d.n_units = static_cast<int64_t>(batch) * ((max_blocks + rla::kDecodeUnitBlocks - 1) / rla::kDecodeUnitBlocks);
-  }
-  const bool f32 = p->out_dtype == RLA_DT_FP32;
-  hipStream_t s = static_cast<hipStream_t>(hip_stream);
-  hipError_t e = rla::launch_decode_items(d, p->kv_block_size, f32, s);
-  if (e != hipSuccess) return hip_status(e, "decode launch");
-
-  rla::FoldArgs f;
-  std::memset(&f, 0, sizeof f);
-  f.part_out = items_out;
-  f.part_lse = items_lse;
-  f.ctx_lens = context_lens;
-  f.out = out;
-  f.lse = lse;
-  f.rows = batch;
-  f.Hq = p->num_q_heads;
-  f.n_parts = static_cast<int32_t>(max_blocks);
-  f.block = p->kv_block_size;
-  f.len_cap = static_cast<int32_t>(cap);
-  e = rla::launch_fold(f, true, f32, s);
-  return hip_status(e, "decode fold launch");
+  return run_decode(p, g, q, k_pool, v_pool, num_pages, page_size, page_table, max_pages_per_seq, context_lens, 0,
+                    host_context_lens, batch, max_context_len, cap, workspace, out, lse,
+                    static_cast<hipStream_t>(hip_stream));
 }
 
 rla_status rla_merge_states(const rla_attn_params* p, const rla_partials* parts, void* out, float* lse,

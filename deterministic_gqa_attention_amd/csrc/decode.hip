@@ -96,7 +96,7 @@ struct BlockRegs {
 };
 
 __device__ __forceinline__ int64_t clamp_len(const DecodeArgs& a, int seq) {
-  int64_t len = a.ctx_lens[seq];
+  int64_t len = a.ctx_lens != nullptr ? a.ctx_lens[seq] : a.uniform_len;
   return len < 0 ? 0 : (len > a.len_cap ? a.len_cap : len);
 }
 
@@ -281,7 +281,9 @@ __global__ __launch_bounds__(kThreads, 2) void decode_items_kernel(const DecodeA
     const int64_t kend = blk1 * BK < len ? blk1 * BK : len;
     const int64_t count = (kend + a.P - 1) / a.P - up.first;
     const int32_t* row = a.page_table + static_cast<int64_t>(seq) * a.max_pages + up.first;
-    for (int64_t t = threadIdx.x; t < count; t += kThreads) ids[t] = row[t];
+    const int32_t id0 = seq * a.max_pages + up.first;  // no table: page i of sequence s is s*max_pages + i
+    for (int64_t t = threadIdx.x; t < count; t += kThreads)
+      ids[t] = a.page_table != nullptr ? row[t] : id0 + static_cast<int32_t>(t);
     __syncthreads();
   }
 

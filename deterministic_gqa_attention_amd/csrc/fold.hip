@@ -30,7 +30,7 @@ __global__ __launch_bounds__(kThreads) void fold_kernel(const FoldArgs a) {
 
   int n;
   if constexpr (DECODE) {
-    int64_t len = a.ctx_lens[row];
+    int64_t len = a.ctx_lens != nullptr ? a.ctx_lens[row] : a.uniform_len;
     len = len < 0 ? 0 : (len > a.len_cap ? a.len_cap : len);
     n = static_cast<int>((len + a.block - 1) / a.block);
   } else {

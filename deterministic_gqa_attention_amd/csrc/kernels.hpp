@@ -52,8 +52,8 @@ struct DecodeArgs {
   const uint16_t* q;          // [Bd][Hq][D]
   const uint16_t* k_pool;     // [num_pages][Hkv][P][D]
   const uint16_t* v_pool;
-  const int32_t* page_table;  // [Bd][max_pages]
-  const int32_t* ctx_lens;    // [Bd]
+  const int32_t* page_table;  // [Bd][max_pages]; null: page i of sequence s is s*max_pages + i
+  const int32_t* ctx_lens;    // [Bd]; null: every sequence has uniform_len keys
   float* items_out;           // [Bd][max_blocks][Hq][D]
   float* items_lse;           // [Bd][max_blocks][Hq]
   int64_t num_pages;
@@ -62,6 +62,7 @@ struct DecodeArgs {
   int32_t unit_blocks;        // KV blocks per workgroup unit
   int32_t compact;
   int64_t n_units;            // units in the grid (per kv head)
+  int32_t uniform_len;        // context length of every sequence when ctx_lens is null
   float c;
 };
 
@@ -70,7 +71,8 @@ struct DecodeArgs {
 struct FoldArgs {
   const float* part_out;      // merge: [n_parts][rows][Hq][D]; decode: items
   const float* part_lse;
-  const int32_t* ctx_lens;    // decode: [Bd] (block count per row); merge: null
+  const int32_t* ctx_lens;    // decode: [Bd] (block count per row), null: uniform_len; merge: null
+  int32_t uniform_len;        // decode: length of every row when ctx_lens is null
   void* out;                  // [rows][Hq][D] bf16 or fp32
   float* lse;                 // [rows][Hq]
   int64_t rows;

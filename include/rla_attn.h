@@ -130,7 +130,12 @@ rla_status rla_attn_prefill(const rla_attn_params* p, const void* q, const void*
  * q_chunk [batch][chunk_len][Hq][128]; k_cache, v_cache [batch][s_max][Hkv][128];
  * out [batch][chunk_len][Hq][128], lse [batch][chunk_len][Hq].
  * Requires cache_len >= 0, chunk_len >= 1, cache_len + chunk_len <= s_max.
- * shard as in rla_attn_prefill (q_begin/q_count relative to the chunk). */
+ * shard as in rla_attn_prefill (q_begin/q_count relative to the chunk).
+ * A chunk of one query without a shard runs as a decode step (the cache read
+ * as a pool of one-key pages: KV blocks spread over many workgroups, block
+ * items folded in order); it takes its item scratch, stream-ordered, from a
+ * device memory pool the library keeps (allocated on first use, reused
+ * after).  The result bits do not depend on the route. */
 rla_status rla_attn_prefill_chunked(const rla_attn_params* p, const void* q_chunk, const void* k_cache,
                                     const void* v_cache, int32_t batch, int32_t chunk_len,
                                     int32_t cache_len, int32_t s_max, const rla_shard* shard, void* out,

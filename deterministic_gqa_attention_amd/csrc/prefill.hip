@@ -443,16 +443,20 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe_kernel(const PrefillArg
   PagedLoader<BK, kWaves> pl;
   if constexpr (PAGED)
     pl.init(a.page_table + static_cast<int64_t>(tm.b) * a.max_pages, a.log2_P, a.kv_len, a.num_pages, a.Hkv, tm.hk);
-  auto issue_k = [&](char* dst, int64_t key0) {
+  // paged: the page ids of block j (ids_cur) and j+1 (ids_next), fetched a
+  // step ahead and before the V loads of the step, so the waits below cover
+  // them and no issue waits for a table read
+  int ids_cur = 0, ids_next = 0;
+  auto issue_k = [&](char* dst, int64_t key0, int ids) {
     if constexpr (PAGED) {
-      pl.template issue<false>(dst, a.k, key0);
+      pl.template issue_with<false>(dst, a.k, key0, ids);
     } else {
       ld.issue_k(dst, w.krs, key0);
     }
   };
-  auto issue_v = [&](char* dst, int64_t key0) {
+  auto issue_v = [&](char* dst, int64_t key0, int ids) {
     if constexpr (PAGED) {
-      pl.template issue<true>(dst, a.v, key0);
+      pl.template issue_with<true>(dst, a.v, key0, ids);
     } else {
       ld.issue_v(dst, w.vrs, key0);
     }
@@ -464,7 +468,8 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe_kernel(const PrefillArg
   // V buffer 1 stands for block -1 in the first step: zeros
   for (int i = threadIdx.x; i < L::kVBytes / 16; i += kThreads)
     *reinterpret_cast<u32x4*>(vbuf + L::kVBytes + 16 * i) = u32x4{0, 0, 0, 0};
-  if (nblk > 0) issue_k(kbuf, 0);
+  if constexpr (PAGED) ids_cur = pl.fetch(0);
+  if (nblk > 0) issue_k(kbuf, 0, ids_cur);
   wait_direct_loads();  // K_0
   lds_barrier();
 
@@ -477,7 +482,8 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe_kernel(const PrefillArg
   // of block j-1 (pending pv+fold when pend).
   auto step = [&](int64_t blk, char* __restrict__ kc, char* __restrict__ vn, const char* __restrict__ vp, P& Pn,
                   FoldIn& inn, const P& Pp, const FoldIn& inp, bool& pend) {
-    if (blk < nblk) issue_v(vn, blk * BK);
+    if constexpr (PAGED) ids_next = pl.fetch((blk + 1) * BK);
+    if (blk < nblk) issue_v(vn, blk * BK, ids_cur);
     const bool sm = blk < nblk && wave_sees<BK>(a, tm, blk);
     f32x16 s[BK / 32];
     if (sm) block_scores_q<BK>(kc, qlane, s);
@@ -485,7 +491,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe_kernel(const PrefillArg
     sched_fence();
     wait_loads_leq<Ld::NI>(cnt(blk));  // V_{j-1} landed (V_j may be in flight)
     lds_barrier();
-    if (blk + 1 < nblk) issue_k(kc, (blk + 1) * BK);
+    if (blk + 1 < nblk) issue_k(kc, (blk + 1) * BK, ids_next);
     if (sm && !wave_full<BK>(a, tm, blk)) apply_mask<BK>(s, static_cast<int>(blk * BK), kvl, a.causal, qpos);
     if (pend && inp.any_move) {
 #pragma unroll
@@ -519,6 +525,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe_kernel(const PrefillArg
     wait_direct_loads();  // K_{j+1} (and V_j) landed
     if constexpr (PAGED) {
       if (blk < nblk && (blk + 1) * BK > a.kv_len) pl.clear_tail(vn, blk * BK, a.kv_len);
+      ids_cur = ids_next;
     }
     lds_barrier();
   };

@@ -121,6 +121,7 @@ struct PagedLoader {
   using L = TileLayout<BK>;
   static constexpr int NI = L::kLoadsPerRegion / NW;
   static_assert(NW % 4 == 0, "swizzle bits must not depend on the load index");
+  static_assert((NI & (NI - 1)) == 0 && NI <= 64, "one id per lane");
   int wave;
   int kbyte0;               // lane's byte offset within its 4-row group (K swizzle)
   int vbyte0;               // the same with the V swizzle
@@ -152,15 +153,34 @@ struct PagedLoader {
     typedef const __attribute__((address_space(4))) int32_t ctab;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const int n = wave + NW * i;
-      const int64_t key = key0 + 4 * n;
-      const int idx = min(static_cast<int>(key >> log2_P), last_idx);
-      int64_t page = ((ctab*)table)[idx];
-      page = page < 0 ? 0 : (page >= num_pages ? num_pages - 1 : page);
-      const int64_t slot = key & ((int64_t{1} << log2_P) - 1);
-      const char* base = reinterpret_cast<const char*>(pool + page * page_elems + head_elems + slot * kHeadDim);
-      direct_load16(reinterpret_cast<const uint16_t*>(base + (V ? vbyte0 : kbyte0)), dst + n * 1024);
+      const int idx = min(static_cast<int>((key0 + 4 * (wave + NW * i)) >> log2_P), last_idx);
+      load_one<V>(dst, pool, key0, i, ((ctab*)table)[idx]);
     }
+  }
+
+  // The page ids of this wave's loads of the block at key0, fetched ahead by
+  // one vector load (lane i < NI: the page of load i), so that issue_with
+  // never waits for a table read: the ids travel with the wave's other
+  // vector loads and are complete once any later load is.
+  __device__ __forceinline__ int fetch(int64_t key0) const {
+    const int i = (threadIdx.x & 63) & (NI - 1);
+    const int idx = min(static_cast<int>((key0 + 4 * (wave + NW * i)) >> log2_P), last_idx);
+    return table[idx];
+  }
+  template <bool V>
+  __device__ __forceinline__ void issue_with(char* dst, const uint16_t* pool, int64_t key0, int ids) const {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) load_one<V>(dst, pool, key0, i, __builtin_amdgcn_readlane(ids, i));
+  }
+
+  template <bool V>
+  __device__ __forceinline__ void load_one(char* dst, const uint16_t* pool, int64_t key0, int i, int64_t page) const {
+    const int n = wave + NW * i;
+    const int64_t key = key0 + 4 * n;
+    page = page < 0 ? 0 : (page >= num_pages ? num_pages - 1 : page);
+    const int64_t slot = key & ((int64_t{1} << log2_P) - 1);
+    const char* base = reinterpret_cast<const char*>(pool + page * page_elems + head_elems + slot * kHeadDim);
+    direct_load16(reinterpret_cast<const uint16_t*>(base + (V ? vbyte0 : kbyte0)), dst + n * 1024);
   }
 
   // Zero the rows at or past kv_len among those this wave loaded for the

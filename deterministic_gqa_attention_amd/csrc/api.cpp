@@ -70,6 +70,12 @@ rla_status check_params(const rla_attn_params* p, bool attention_call, int* grou
   return RLA_OK;
 }
 
+// The kernels address one head's K/V rows and one head's Q rows with 32-bit
+// byte offsets (buffer resources).
+bool fits_32bit_offsets(int64_t rows, int heads) {
+  return rows <= 0 || (rows - 1) * heads * rla::kHeadDimPublic * 2 + rla::kHeadDimPublic * 2 <= 0x7fffffff;
+}
+
 // c = softmax_scale * log2(e), rounded once to fp32; every kernel receives it.
 float score_scale(const rla_attn_params* p) {
   return static_cast<float>(static_cast<double>(p->softmax_scale) * 1.4426950408889634073599);
@@ -84,6 +90,10 @@ rla_status prefill_common(const rla_attn_params* p, const void* q, const void* k
   if (st != RLA_OK) return st;
   if (q == nullptr || k == nullptr || v == nullptr) return fail(RLA_ERR_NULL_POINTER, "q, k or v is NULL");
   const int Hq = p->num_q_heads, Hkv = p->num_kv_heads, D = rla::kHeadDimPublic;
+
+  if (!fits_32bit_offsets(kv_len, p->num_kv_heads) || !fits_32bit_offsets(q_rows, Hq))
+    return fail(RLA_ERR_UNSUPPORTED, "sequence too long: one head's rows must span < 2 GiB (q_rows=%d, kv_len=%lld)",
+                q_rows, (long long)kv_len);
 
   rla::PrefillArgs a;
   std::memset(&a, 0, sizeof a);
@@ -335,6 +345,8 @@ rla_status rla_attn_prefill_paged(const rla_attn_params* p, const void* q_chunk,
                 (long long)max_pages_per_seq * page_size, (long long)kv_len);
   if (kv_len > 0x7fffffff) return fail(RLA_ERR_BAD_SHAPE, "cache_len+chunk_len exceeds int32 positions");
   const int Hq = p->num_q_heads, D = rla::kHeadDimPublic;
+  if (!fits_32bit_offsets(chunk_len, Hq))
+    return fail(RLA_ERR_UNSUPPORTED, "chunk too long: one head's query rows must span < 2 GiB");
 
   rla::PrefillArgs a;
   std::memset(&a, 0, sizeof a);

@@ -85,6 +85,16 @@ def test_chunked_rejects_overflowing_cache(lib):
     assert st == 2
 
 
+def test_prefill_rejects_rows_beyond_32bit_offsets(lib):
+    """One head's Q or K/V rows must span < 2 GiB (32-bit buffer offsets)."""
+    p = _params()  # Hq=32: 2^18 query rows of one head span 2 GiB
+    st = lib.rla_attn_prefill(ctypes.byref(p), FAKE, FAKE, FAKE, 1, (1 << 18) + 1, None, FAKE, FAKE, None)
+    assert st == 3 and "2 GiB" in lib.rla_last_error().decode()
+    st = lib.rla_attn_prefill_chunked(ctypes.byref(p), FAKE, FAKE, FAKE, 1, 16, (1 << 20), (1 << 20) + 16, None,
+                                      FAKE, FAKE, None)  # Hkv=8: 2^20 keys span 2 GiB
+    assert st == 3 and "2 GiB" in lib.rla_last_error().decode()
+
+
 def test_paged_prefill_rejects_bad_args(lib):
     p = _params()
     # (num_pages, page_size, max_pages, batch, chunk, cache) -> status

@@ -11,8 +11,8 @@ Two independent implementations live here:
 * ``brute.py``: a numpy FP64 brute force for tiny shapes that exponentiates raw
   scores without any max subtraction.  It exists only to pin the C oracle.
 """
-from .core import (ORACLE_LIB, attention, block_states, build, decode_paged, merge,
-                   oracle_threads)
+from .core import (ORACLE_LIB, attention, attention_backward, block_states, build, decode_paged,
+                   merge, oracle_threads)
 
-__all__ = ["ORACLE_LIB", "attention", "block_states", "build", "decode_paged", "merge",
-           "oracle_threads"]
+__all__ = ["ORACLE_LIB", "attention", "attention_backward", "block_states", "build",
+           "decode_paged", "merge", "oracle_threads"]

@@ -21,7 +21,13 @@ def bf16_bits_to_f64(a: np.ndarray) -> np.ndarray:
 def attention(q, k, v, *, scale, causal=True, pos0=0, kv_len=None):
     """q uint16 [B, Sq, Hq, D]; k, v uint16 [B, Skv, Hkv, D] -> (out, lse) float64
     with out [B, Sq, Hq, D] and lse [B, Sq, Hq]."""
-    Q, K, V = bf16_bits_to_f64(q), bf16_bits_to_f64(k), bf16_bits_to_f64(v)
+    return attention_f64(bf16_bits_to_f64(q), bf16_bits_to_f64(k), bf16_bits_to_f64(v),
+                         scale=scale, causal=causal, pos0=pos0, kv_len=kv_len)
+
+
+def attention_f64(Q, K, V, *, scale, causal=True, pos0=0, kv_len=None):
+    """The same definition on real-valued float64 inputs (any values, not only
+    bf16 ones), so that it can be differentiated numerically."""
     B, Sq, Hq, D = Q.shape
     Skv, Hkv = K.shape[1], K.shape[2]
     kv_len = Skv if kv_len is None else kv_len

@@ -292,3 +292,130 @@ int orc_decode_paged(const uint16_t* q, const uint16_t* k_pool, const uint16_t* 
     }
     return bad ? -1 : 0;
 }
+
+/*
+ * Gradient of attention (the backward pass: [P3] "PR stack", the
+ * prefill/chunked-prefill backward reference for dQ/dK/dV; [P3] "Status" and
+ * "Acceptance": dQ, dK and dV are strict outputs alongside Out and LSE).
+ *
+ * Definition.  For the forward of orc_attention (full key range) and an
+ * upstream gradient dOut of Out (the LSE output receives no gradient), the
+ * exact partial derivatives of  Lsum = sum_{rows, h, d} Out * dOut  are, per
+ * query row i of q head h with key set J(i) and probabilities
+ * P_ij = exp(s_ij - LSE_i):
+ *   dP_ij   = sum_d dOut[i,h,d] * V[j,hk,d]
+ *   Delta_i = sum_{j in J(i)} P_ij * dP_ij
+ *   dS_ij   = P_ij * (dP_ij - Delta_i)             (softmax Jacobian)
+ *   dQ[i,h] = scale * sum_j dS_ij * K[j,hk]
+ *   dK[j,hk] += scale * dS_ij * Q[i,h]             (summed over the group's q heads)
+ *   dV[j,hk] += P_ij * dOut[i,h]
+ * Keys outside every row's key set get dK = dV = 0; a row with no key gets
+ * dQ = 0.  The sums run in plain row and key order in double precision.
+ *
+ * Optional error-bound magnitudes (any may be NULL): with
+ *   |dP|_ij = sum_d |dOut[i,h,d]| |V[j,hk,d]|,   delta_i = sum_j P_ij |dP|_ij,
+ *   G_ij    = scale * (|P_ij (dP_ij - Delta_i)| + P_ij (delta_i + |dP|_ij)),
+ * mag_dq[i,h,d] = sum_j G_ij |K[j,hk,d]|, mag_dk[j,hk,d] = sum_{i,h} G_ij |Q[i,h,d]|
+ * and mag_dv[j,hk,d] = sum_{i,h} P_ij |dOut[i,h,d]|.  They are the sums of
+ * absolute values that a bound on a finite-precision evaluation scales: G_ij
+ * bounds |dS_ij| plus the part of dS_ij that an error in Delta_i (relative to
+ * delta_i) or in dP_ij (relative to |dP|_ij) can move.
+ *
+ * Layouts: q, dout [B][Sq][Hq][D]; k, v [B][Skv][Hkv][D] (bf16 bits);
+ * dq and mag_dq [B][Sq][Hq][D], dk, dv, mag_dk, mag_dv [B][Skv][Hkv][D]
+ * (double).  Query t sits at position pos0 + t.  Returns 0, or -1 on bad
+ * arguments.
+ */
+int orc_attention_backward(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                           const uint16_t* dout, int B, int Sq, int Skv, int Hq, int Hkv, int D,
+                           int64_t pos0, int causal, int64_t kv_len, double scale,
+                           double* dq, double* dk, double* dv,
+                           double* mag_dq, double* mag_dk, double* mag_dv) {
+    if (B <= 0 || Sq < 0 || Skv < 0 || Hq <= 0 || Hkv <= 0 || D <= 0) return -1;
+    if (Hq % Hkv != 0 || kv_len > Skv || kv_len < 0) return -1;
+    const int group = Hq / Hkv;
+    int bad = 0;
+    memset(dq, 0, sizeof(double) * (size_t)B * Sq * Hq * D);
+    memset(dk, 0, sizeof(double) * (size_t)B * Skv * Hkv * D);
+    memset(dv, 0, sizeof(double) * (size_t)B * Skv * Hkv * D);
+    if (mag_dq) memset(mag_dq, 0, sizeof(double) * (size_t)B * Sq * Hq * D);
+    if (mag_dk) memset(mag_dk, 0, sizeof(double) * (size_t)B * Skv * Hkv * D);
+    if (mag_dv) memset(mag_dv, 0, sizeof(double) * (size_t)B * Skv * Hkv * D);
+
+    /* One (batch, kv head) per iteration: every write below lands in that
+     * pair's rows, so iterations never touch the same memory. */
+#pragma omp parallel
+    {
+        const size_t n = (size_t)(Skv > 0 ? Skv : 1);
+        double* s = (double*)malloc(sizeof(double) * n);
+        double* dp = (double*)malloc(sizeof(double) * n);
+        double* adp = (double*)malloc(sizeof(double) * n);
+        if (s == NULL || dp == NULL || adp == NULL) {
+#pragma omp atomic write
+            bad = 1;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t pair = 0; pair < (int64_t)B * Hkv; ++pair) {
+            if (s == NULL || dp == NULL || adp == NULL) continue;
+            const int64_t b = pair / Hkv;
+            const int hk = (int)(pair % Hkv);
+            for (int h = hk * group; h < (hk + 1) * group; ++h) {
+                for (int64_t t = 0; t < Sq; ++t) {
+                    const int64_t pos = pos0 + t;
+                    int64_t hi = kv_len;
+                    if (causal && hi > pos + 1) hi = pos + 1;
+                    if (hi <= 0) continue;
+                    const int64_t qoff = ((b * Sq + t) * Hq + h) * (int64_t)D;
+                    const uint16_t* qrow = q + qoff;
+                    const uint16_t* grow = dout + qoff;
+                    double m = -INFINITY;
+                    for (int64_t j = 0; j < hi; ++j) {
+                        const int64_t koff = ((b * Skv + j) * Hkv + hk) * (int64_t)D;
+                        double dot = 0.0, g = 0.0, ag = 0.0;
+                        for (int d = 0; d < D; ++d) {
+                            dot += bf16_to_double(qrow[d]) * bf16_to_double(k[koff + d]);
+                            g += bf16_to_double(grow[d]) * bf16_to_double(v[koff + d]);
+                            ag += fabs(bf16_to_double(grow[d])) * fabs(bf16_to_double(v[koff + d]));
+                        }
+                        s[j] = scale * dot;
+                        dp[j] = g;
+                        adp[j] = ag;
+                        if (s[j] > m) m = s[j];
+                    }
+                    double sum = 0.0;
+                    for (int64_t j = 0; j < hi; ++j) sum += exp(s[j] - m);
+                    const double L = m + log(sum);
+                    /* s[j] becomes P_ij from here on. */
+                    double delta = 0.0, adelta = 0.0;
+                    for (int64_t j = 0; j < hi; ++j) {
+                        s[j] = exp(s[j] - L);
+                        delta += s[j] * dp[j];
+                        adelta += s[j] * adp[j];
+                    }
+                    double* dqrow = dq + qoff;
+                    for (int64_t j = 0; j < hi; ++j) {
+                        const double p = s[j];
+                        const double ds = p * (dp[j] - delta);
+                        const double gmag = scale * (fabs(ds) + p * (adelta + adp[j]));
+                        const int64_t koff = ((b * Skv + j) * Hkv + hk) * (int64_t)D;
+                        for (int d = 0; d < D; ++d) {
+                            const double kd = bf16_to_double(k[koff + d]);
+                            const double qd = bf16_to_double(qrow[d]);
+                            const double gd = bf16_to_double(grow[d]);
+                            dqrow[d] += scale * ds * kd;
+                            dk[koff + d] += scale * ds * qd;
+                            dv[koff + d] += p * gd;
+                            if (mag_dq) mag_dq[qoff + d] += gmag * fabs(kd);
+                            if (mag_dk) mag_dk[koff + d] += gmag * fabs(qd);
+                            if (mag_dv) mag_dv[koff + d] += p * fabs(gd);
+                        }
+                    }
+                }
+            }
+        }
+        free(s);
+        free(dp);
+        free(adp);
+    }
+    return bad ? -1 : 0;
+}

@@ -268,6 +268,124 @@ def pin_decode_equals_prefill_last_row(lib_path=None):
     _bits_equal(dl, dl2, "relocated lse")
 
 
+# ------------------------------------------------------------------ backward pins
+
+
+def pin_backward_finite_differences(lib_path=None):
+    """The oracle's dQ/dK/dV equal central differences of the separately written
+    numpy forward (``brute.attention_f64``) of  sum(Out * dOut),  element by
+    element: causal GQA, a chunk after cached keys, and non-causal with a short
+    kv_len."""
+    cases = [
+        # B, Sq, Skv, Hq, Hkv, D, causal, pos0, kv_len
+        (1, 6, 6, 4, 2, 4, True, 0, 6),
+        (2, 3, 7, 2, 1, 4, True, 4, 7),
+        (1, 4, 6, 2, 2, 3, False, 0, 5),
+    ]
+    h = 1e-6
+    for n, (B, Sq, Skv, Hq, Hkv, D, causal, pos0, kv_len) in enumerate(cases):
+        q, k = _rand(400 + n, (B, Sq, Hq, D)), _rand(410 + n, (B, Skv, Hkv, D))
+        v, do = _rand(420 + n, (B, Skv, Hkv, D)), _rand(430 + n, (B, Sq, Hq, D))
+        scale = 0.45
+        grads = oracle.attention_backward(q, k, v, do, scale=scale, causal=causal, pos0=pos0,
+                                          kv_len=kv_len, lib_path=lib_path)
+        xs = [brute.bf16_bits_to_f64(a) for a in (q, k, v)]
+        G = brute.bf16_bits_to_f64(do)
+
+        def loss(a):
+            o, _ = brute.attention_f64(*a, scale=scale, causal=causal, pos0=pos0, kv_len=kv_len)
+            return float((o * G).sum())
+
+        for w, name in enumerate("qkv"):
+            num = np.zeros_like(xs[w])
+            for idx in np.ndindex(xs[w].shape):
+                a = list(xs)
+                a[w] = xs[w].copy()
+                a[w][idx] += h
+                lp = loss(a)
+                a[w][idx] -= 2 * h
+                num[idx] = (lp - loss(a)) / (2 * h)
+            _close(grads[w], num, tol=1e-7, what=f"d{name} vs finite differences, case {n}")
+
+
+def pin_backward_shift_invariances(lib_path=None):
+    """Softmax ignores a common shift of a row's scores, so adding one vector to
+    every key changes nothing: sum_j dK_j = 0.  Every probability row sums to 1,
+    so sum_j dV_j is the sum of dOut over the rows (and group heads) that see at
+    least one key."""
+    B, S, Hq, Hkv, D = 2, 9, 4, 2, 8
+    q, k = _rand(441, (B, S, Hq, D)), _rand(442, (B, S, Hkv, D), 2.0)
+    v, do = _rand(443, (B, S, Hkv, D)), _rand(444, (B, S, Hq, D))
+    for causal, pos0, kv_len, Sq in ((True, 0, S, S), (True, 5, S, 4), (False, 0, 6, S)):
+        qq, dd = q[:, :Sq], do[:, :Sq]
+        dq, dk, dv = oracle.attention_backward(qq, k, v, dd, scale=0.4, causal=causal, pos0=pos0,
+                                               kv_len=kv_len, lib_path=lib_path)
+        _close(dk.sum(axis=1), 0.0, tol=1e-12, what="sum of dK")
+        G = brute.bf16_bits_to_f64(dd).reshape(B, Sq, Hkv, Hq // Hkv, D).sum(axis=(1, 3))
+        _close(dv.sum(axis=1), G, tol=1e-12, what="sum of dV")
+        assert np.abs(dk).max() > 1e-3, "dK must not vanish"
+
+
+def pin_backward_single_key(lib_path=None):
+    """A row that sees exactly one key has P = 1 and dS = 0, so its dQ is exactly
+    0; with a single token, dK = 0 and dV_0 is the sum of dOut over the group."""
+    B, Hq, Hkv, D = 2, 6, 3, 8
+    q, k = _rand(451, (B, 1, Hq, D)), _rand(452, (B, 1, Hkv, D))
+    v, do = _rand(453, (B, 1, Hkv, D)), _rand(454, (B, 1, Hq, D))
+    dq, dk, dv = oracle.attention_backward(q, k, v, do, scale=0.3, lib_path=lib_path)
+    assert np.array_equal(dq, np.zeros_like(dq)), "single-key dQ must be exactly 0"
+    assert np.array_equal(dk, np.zeros_like(dk)), "single-key dK must be exactly 0"
+    G = brute.bf16_bits_to_f64(do).reshape(B, 1, Hkv, Hq // Hkv, D).sum(axis=3)
+    _close(dv, G, tol=1e-15, what="single-key dV")
+    # rows of a longer causal sequence: row 0 sees one key
+    q, k = _rand(455, (B, 5, Hq, D)), _rand(456, (B, 5, Hkv, D))
+    v, do = _rand(457, (B, 5, Hkv, D)), _rand(458, (B, 5, Hq, D))
+    dq, dk, dv = oracle.attention_backward(q, k, v, do, scale=0.3, lib_path=lib_path)
+    assert np.array_equal(dq[:, 0], np.zeros_like(dq[:, 0])), "row 0 dQ must be exactly 0"
+    assert np.abs(dq[:, 1:]).max() > 1e-3, "later rows must have a gradient"
+
+
+def pin_backward_gqa_and_chunks(lib_path=None):
+    """GQA gradients equal MHA gradients on replicated K/V heads with dK/dV summed
+    over each group; a chunk's dQ rows equal the full call's rows (bitwise: the
+    same operations), and the chunks' dK/dV add up to the full dK/dV."""
+    B, S, Hq, Hkv, D = 1, 12, 8, 2, 8
+    g = Hq // Hkv
+    q, k = _rand(461, (B, S, Hq, D)), _rand(462, (B, S, Hkv, D))
+    v, do = _rand(463, (B, S, Hkv, D)), _rand(464, (B, S, Hq, D))
+    dq, dk, dv = oracle.attention_backward(q, k, v, do, scale=0.35, lib_path=lib_path)
+    mq, mk, mv = oracle.attention_backward(q, np.repeat(k, g, axis=2), np.repeat(v, g, axis=2), do,
+                                           scale=0.35, lib_path=lib_path)
+    _close(dq, mq, tol=1e-13, what="GQA dQ")
+    _close(dk, mk.reshape(B, S, Hkv, g, D).sum(axis=3), tol=1e-13, what="GQA dK")
+    _close(dv, mv.reshape(B, S, Hkv, g, D).sum(axis=3), tol=1e-13, what="GQA dV")
+    sk, sv = np.zeros_like(dk), np.zeros_like(dv)
+    for c, C in ((0, 5), (5, 1), (6, 6)):
+        cq, ck, cv = oracle.attention_backward(q[:, c:c + C], k, v, do[:, c:c + C], scale=0.35,
+                                               pos0=c, kv_len=c + C, lib_path=lib_path)
+        _bits_equal(cq, dq[:, c:c + C], f"chunk {c}+{C} dQ")
+        sk += ck
+        sv += cv
+    _close(sk, dk, tol=1e-13, what="chunked dK sum")
+    _close(sv, dv, tol=1e-13, what="chunked dV sum")
+
+
+def pin_backward_magnitudes(lib_path=None):
+    """The error-bound magnitudes dominate the gradients they bound (triangle
+    inequality), and vanish exactly where the gradient has no term."""
+    B, S, Hq, Hkv, D = 1, 7, 4, 2, 8
+    q, k = _rand(471, (B, S, Hq, D)), _rand(472, (B, S, Hkv, D))
+    v, do = _rand(473, (B, S, Hkv, D)), _rand(474, (B, S, Hq, D))
+    dq, dk, dv, mq, mk, mv = oracle.attention_backward(q, k, v, do, scale=0.3, kv_len=5,
+                                                       causal=False, mags=True, lib_path=lib_path)
+    for grad, mag, name in ((dq, mq, "dQ"), (dk, mk, "dK"), (dv, mv, "dV")):
+        assert (mag >= np.abs(grad) * (1 - 1e-12)).all(), f"{name} magnitude below |gradient|"
+    assert not mk[:, 5:].any() and not mv[:, 5:].any(), "keys past kv_len carry no magnitude"
+    assert mq.min() > 0
+
+
 ALL_PINS = [pin_brute_force, pin_single_key_row, pin_uniform_scores, pin_constant_v,
             pin_two_key_closed_form, pin_merge_identity, pin_merge_permutation, pin_causality,
-            pin_gqa_replication, pin_chunk_equals_full, pin_decode_equals_prefill_last_row]
+            pin_gqa_replication, pin_chunk_equals_full, pin_decode_equals_prefill_last_row,
+            pin_backward_finite_differences, pin_backward_shift_invariances,
+            pin_backward_single_key, pin_backward_gqa_and_chunks, pin_backward_magnitudes]

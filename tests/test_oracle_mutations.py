@@ -44,6 +44,17 @@ MUTATIONS = [
      "const uint16_t* krow = k_pool + ((page * Hkv + hk) * P + (j + 1) % P) * (int64_t)D;", 0),
     ("decode_drops_current_token", "for (int64_t j = 0; j < len; ++j) sum += exp(s[j] - m);",
      "for (int64_t j = 0; j < len - 1; ++j) sum += exp(s[j] - m);", 0),
+    ("bwd_delta_dropped", "const double ds = p * (dp[j] - delta);", "const double ds = p * dp[j];", 0),
+    ("bwd_delta_unweighted", "delta += s[j] * dp[j];", "delta += dp[j];", 0),
+    ("bwd_dq_scale_dropped", "dqrow[d] += scale * ds * kd;", "dqrow[d] += ds * kd;", 0),
+    ("bwd_dk_sign", "dk[koff + d] += scale * ds * qd;", "dk[koff + d] -= scale * ds * qd;", 0),
+    ("bwd_dv_uses_ds", "dv[koff + d] += p * gd;", "dv[koff + d] += ds * gd;", 0),
+    ("bwd_dp_uses_k", "g += bf16_to_double(grow[d]) * bf16_to_double(v[koff + d]);",
+     "g += bf16_to_double(grow[d]) * bf16_to_double(k[koff + d]);", 0),
+    ("bwd_causal_off_by_one", "if (causal && hi > pos + 1) hi = pos + 1;",
+     "if (causal && hi > pos) hi = pos;", 1),
+    ("bwd_wrong_group", "for (int h = hk * group; h < (hk + 1) * group; ++h) {",
+     "for (int h = hk; h < Hq; h += Hkv) {", 0),
 ]
 
 

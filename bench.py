@@ -179,6 +179,40 @@ def reported_legs(api, up, stream):
     return res
 
 
+def backward_leg(api, cfg, qd, kd, vd, up, stream, steps):
+    """Backward (dQ, dK, dV) of the same causal prefill: pre-pass, dQ and dK/dV
+    launches timed together with events on the launch stream.  Algorithmic
+    flops: the five products QK^T, dOut V^T, P^T dOut, dS^T Q, dS K over the
+    unmasked pairs, 2.5x the forward's."""
+    import torch
+    do = up(gen.dout_inputs(cfg))
+    out, lse = api.prefill(qd, kd, vd, block=cfg.block)
+    dq = torch.empty(qd.shape, dtype=torch.float32, device=qd.device)
+    dk = torch.zeros(kd.shape, dtype=torch.float32, device=qd.device)
+    dv = torch.zeros(kd.shape, dtype=torch.float32, device=qd.device)
+
+    def call():
+        api.backward(qd, kd, vd, out, lse, do, scale=cfg.softmax_scale, dq=dq, dk=dk, dv=dv)
+
+    for _ in range(2):
+        call()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    flops = 2.5 * cfg.flops()
+    del do, out, lse, dq, dk, dv
+    torch.cuda.empty_cache()
+    return {"tflops": round(flops / (ms * 1e-3) / 1e12, 2), "ms": round(ms, 4),
+            "frac_of_peak": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4), "flop_per_step": flops,
+            "workload": "backward of causal prefill B=4 S=4096 Hq=32 Hkv=8 D=128, bf16 in, fp32 dQ/dK/dV"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -189,7 +223,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-reported", action="store_true", help="skip the long-context and chunked-replay legs")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--only", choices=["prefill", "decode", "copy"], default=None,
+    ap.add_argument("--only", choices=["prefill", "decode", "copy", "backward"], default=None,
                     help="run one leg only (for profiler and counter runs)")
     ap.add_argument("--summarize", metavar="DIR", default=None,
                     help="write profiles/*.md from the rocprofv3 CSVs under DIR (no GPU work)")
@@ -214,7 +248,7 @@ def main():
     q, k, v = gen.prefill_inputs(cfg)
     dcfg = gen.CFG4
     d = None
-    if not args.no_decode and args.only != "prefill":
+    if not args.no_decode and args.only in (None, "decode"):
         log("generating paged-decode inputs")
         d = gen.decode_inputs(dcfg)
 
@@ -237,6 +271,11 @@ def main():
     stream = torch.cuda.current_stream(dev)
     flops = cfg.flops()
 
+    if args.only == "backward":
+        log("backward")
+        print(json.dumps({"only": "backward", "backward": backward_leg(api, cfg, qd, kd, vd, up, stream,
+                                                                       max(args.steps, 1))}))
+        return
     if args.only == "decode":
         args.steps = 0
     log("prefill warmup")
@@ -276,6 +315,11 @@ def main():
     if args.only is None:
         drift_batch, drift_cp = invariance_probe(api, cfg, qd, kd, vd, out, dev)
         log(f"invariance drift: batch {drift_batch}, CP=2 reversed {drift_cp}")
+    backward = None
+    if args.only is None:
+        log("backward")
+        backward = backward_leg(api, cfg, qd, kd, vd, up, stream, 10)
+        log(f"backward {backward['ms']:.3f} ms, {backward['tflops']:.1f} TFLOP/s")
     del qd, kd, vd, out
     torch.cuda.empty_cache()
     decode = decode_leg(args, api, d, dcfg, up, dev, stream) if d is not None else None
@@ -295,6 +339,7 @@ def main():
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": profile_traffic(PREFILL_PROFILE),
                      "kernel_ms": round(kern_ms, 4)},
         "decode": decode,
+        "backward": backward,
         "invariance": {"batch_alone_vs_batch": drift_batch, "cp2_reversed_arrival": drift_cp},
         "reported": reported,
         "cpu_baseline": base,

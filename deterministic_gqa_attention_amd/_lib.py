@@ -20,7 +20,8 @@ RLA_MAX_PARTS = 512
 
 # Every function include/rla_attn.h declares.
 EXPORTS = ("rla_attn_prefill", "rla_attn_prefill_chunked", "rla_attn_prefill_paged", "rla_attn_decode_paged",
-           "rla_merge_states", "rla_decode_workspace_bytes", "rla_last_error", "rla_core_id")
+           "rla_merge_states", "rla_attn_backward", "rla_decode_workspace_bytes", "rla_last_error",
+           "rla_core_id")
 
 
 class RlaParams(ctypes.Structure):
@@ -72,6 +73,8 @@ def load(path: str = LIB_PATH):
     lib.rla_attn_decode_paged.argtypes = [pp, P, P, P, i64, i32, P, i32, P, ctypes.POINTER(ctypes.c_int32),
                                           i32, i32, P, sz, P, P, P]
     lib.rla_attn_decode_paged.restype = ctypes.c_int
+    lib.rla_attn_backward.argtypes = [pp, P, P, P, P, P, P, i32, i32, i32, i32, i32, P, P, P, P]
+    lib.rla_attn_backward.restype = ctypes.c_int
     lib.rla_merge_states.argtypes = [pp, ctypes.POINTER(RlaPartials), P, P, P]
     lib.rla_merge_states.restype = ctypes.c_int
     lib.rla_decode_workspace_bytes.argtypes = [pp, i32, i32]

@@ -15,8 +15,8 @@ import torch
 from . import _lib
 from ._lib import RLAError, RlaParams, RlaPartials, RlaShard
 
-__all__ = ["RLAError", "core_id", "prefill", "prefill_chunked", "emit_partials", "merge_states",
-           "decode_paged", "decode_workspace_bytes", "params"]
+__all__ = ["RLAError", "core_id", "prefill", "prefill_chunked", "prefill_paged", "emit_partials",
+           "merge_states", "decode_paged", "decode_workspace_bytes", "backward", "params"]
 
 _OUT_DT = {torch.bfloat16: _lib.RLA_DT_BF16, torch.float32: _lib.RLA_DT_FP32}
 _ORDER = {"global_block_index": _lib.RLA_ORDER_GLOBAL_BLOCK_INDEX, "arrival": _lib.RLA_ORDER_ARRIVAL}
@@ -120,6 +120,35 @@ def prefill_paged(q_chunk, k_pool, v_pool, page_table, *, cache_len, block, out_
         _dev(v_pool, "v_pool", torch.bfloat16, 4), num_pages, P, _dev(page_table, "page_table", torch.int32, 2),
         page_table.shape[1], B, C, int(cache_len), out.data_ptr(), lse.data_ptr(), _stream(q_chunk.device)))
     return out, lse
+
+
+def backward(q, k, v, out, lse, dout, *, cache_len=0, causal=True, scale=None, dq=None, dk=None, dv=None,
+             accumulate=False):
+    """dQ, dK, dV of Out for (chunked) prefill.
+
+    q, dout [B,C,Hq,128] bf16; k, v [B,S_max,Hkv,128] bf16 (keys [0, cache_len+C)
+    used); out [B,C,Hq,128] (bf16 or fp32, the forward output); lse [B,C,Hq] fp32.
+    Returns (dq [B,C,Hq,128], dk, dv [B,S_max,Hkv,128]) in fp32; dk/dv rows past
+    cache_len+C are left as given (zeros when allocated here).  With
+    ``accumulate`` the call adds to the given dk/dv."""
+    B, C, Hq, D = q.shape
+    S_max, Hkv = k.shape[1], k.shape[2]
+    if out.dtype not in _OUT_DT:
+        raise ValueError(f"out must be bf16 or fp32, got {out.dtype}")
+    p = params(Hq, Hkv, block=128, out_dtype=out.dtype, causal=causal, scale=scale, head_dim=D)
+    dq = torch.empty((B, C, Hq, D), dtype=torch.float32, device=q.device) if dq is None else dq
+    if dk is None:
+        dk = torch.zeros((B, S_max, Hkv, D), dtype=torch.float32, device=q.device)
+    if dv is None:
+        dv = torch.zeros((B, S_max, Hkv, D), dtype=torch.float32, device=q.device)
+    lib = _lib.load()
+    _lib.check(lib.rla_attn_backward(
+        ctypes.byref(p), _dev(q, "q", torch.bfloat16, 4), _dev(k, "k", torch.bfloat16, 4),
+        _dev(v, "v", torch.bfloat16, 4), _dev(out, "out", out.dtype, 4), _dev(lse, "lse", torch.float32, 3),
+        _dev(dout, "dout", torch.bfloat16, 4), B, C, int(cache_len), S_max, int(bool(accumulate)),
+        _dev(dq, "dq", torch.float32, 4), _dev(dk, "dk", torch.float32, 4), _dev(dv, "dv", torch.float32, 4),
+        _stream(q.device)))
+    return dq, dk, dv
 
 
 def emit_partials(q, k, v, kv_blocks, *, block, out_dtype=torch.bfloat16, causal=True, scale=None, q_begin=0,

@@ -419,6 +419,71 @@ rla_status rla_attn_decode_paged(const rla_attn_params* p, const void* q, const 
                     static_cast<hipStream_t>(hip_stream));
 }
 
+rla_status rla_attn_backward(const rla_attn_params* p, const void* q, const void* k, const void* v,
+                             const void* out, const float* lse, const void* dout, int32_t batch,
+                             int32_t q_rows, int32_t cache_len, int32_t s_max, int32_t accumulate,
+                             float* dq, float* dk, float* dv, void* hip_stream) {
+  int g = 0;
+  rla_status st = check_params(p, true, &g);
+  if (st != RLA_OK) return st;
+  if (q == nullptr || k == nullptr || v == nullptr || out == nullptr || lse == nullptr || dout == nullptr ||
+      dq == nullptr || dk == nullptr || dv == nullptr)
+    return fail(RLA_ERR_NULL_POINTER, "a required pointer is NULL");
+  if (batch < 1 || q_rows < 1 || cache_len < 0 || s_max < 1 || static_cast<int64_t>(cache_len) + q_rows > s_max)
+    return fail(RLA_ERR_BAD_SHAPE, "need batch>=1, q_rows>=1, cache_len>=0, cache_len+q_rows<=s_max "
+                "(got %d, %d, %d, %d)", batch, q_rows, cache_len, s_max);
+  if (accumulate != 0 && accumulate != 1) return fail(RLA_ERR_BAD_SHAPE, "accumulate must be 0 or 1");
+  const int Hq = p->num_q_heads, Hkv = p->num_kv_heads, D = rla::kHeadDimPublic;
+  const int64_t kv_len = static_cast<int64_t>(cache_len) + q_rows;
+  // Sq_pad = q_rows rounded up to the 64-row tile; its rows must fit the
+  // 32-bit row offsets too.
+  const int64_t sq_pad = (static_cast<int64_t>(q_rows) + 63) / 64 * 64;
+  if (!fits_32bit_offsets(kv_len, Hkv) || !fits_32bit_offsets(sq_pad, Hq) || sq_pad > 0x7fffffff)
+    return fail(RLA_ERR_UNSUPPORTED, "sequence too long: one head's rows must span < 2 GiB (q_rows=%d, kv_len=%lld)",
+                q_rows, (long long)kv_len);
+
+  rla::BackwardArgs a;
+  std::memset(&a, 0, sizeof a);
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.out = out;
+  a.lse = lse;
+  a.dout = static_cast<const uint16_t*>(dout);
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.q_bstride = static_cast<int64_t>(q_rows) * Hq * D;
+  a.kv_bstride = static_cast<int64_t>(s_max) * Hkv * D;
+  a.pos0 = cache_len;
+  a.kv_len = kv_len;
+  a.B = batch;
+  a.Sq = q_rows;
+  a.Sq_pad = static_cast<int32_t>(sq_pad);
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.G = g;
+  a.hpw = g < 4 ? g : 4;
+  a.hsubs = g / a.hpw;
+  a.n_qtiles = static_cast<int32_t>(sq_pad / 64);
+  a.n_kblocks = static_cast<int32_t>((kv_len + 127) / 128);
+  a.causal = p->causal;
+  a.accumulate = accumulate;
+  a.c = score_scale(p);
+  a.scale = p->softmax_scale;
+
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  const size_t ws_bytes = static_cast<size_t>(batch) * Hq * 2 * static_cast<size_t>(sq_pad) * sizeof(float);
+  void* ws = nullptr;
+  hipError_t e = scratch_alloc(&ws, ws_bytes, s);
+  if (e != hipSuccess) return hip_status(e, "backward scratch");
+  a.ws = static_cast<float*>(ws);
+  e = rla::launch_backward(a, p->out_dtype == RLA_DT_FP32, s);
+  const hipError_t ef = hipFreeAsync(ws, s);
+  if (e != hipSuccess) return hip_status(e, "backward launch");
+  return hip_status(ef, "backward scratch free");
+}
+
 rla_status rla_merge_states(const rla_attn_params* p, const rla_partials* parts, void* out, float* lse,
                             void* hip_stream) {
   rla_status st = check_params(p, false, nullptr);

@@ -83,7 +83,40 @@ struct FoldArgs {
   uint16_t order[kMaxParts];  // merge: part indices in fold order
 };
 
+// Backward (dQ, dK, dV of Out).  Query row t of batch b sits at position
+// pos0 + t and attends keys [0, kv_len) (key <= position when causal).
+// q, out, dout, dq share q's layout (b*q_bstride + (t*Hq + h)*D); k, v, dk, dv
+// share k's layout (b*kv_bstride + (key*Hkv + hk)*D).  ws: [B][Hq][2][Sq_pad]
+// scratch (LSE*log2 e, then Delta, per row).
+struct BackwardArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const void* out;           // forward Out, bf16 or fp32
+  const float* lse;          // forward LSE [B][Sq][Hq], natural log
+  const uint16_t* dout;      // gradient of Out, bf16
+  float* ws;
+  float* dq;                 // fp32
+  float* dk;                 // fp32; read first when accumulate is set
+  float* dv;
+  int64_t q_bstride;
+  int64_t kv_bstride;
+  int64_t pos0;
+  int64_t kv_len;
+  int32_t B, Sq, Sq_pad, Hq, Hkv, G;
+  int32_t hpw;               // dQ kernel: q heads per workgroup (min(G, 4))
+  int32_t hsubs;             // dQ kernel: workgroups per group (G / hpw)
+  int32_t n_qtiles;          // ceil(Sq / 64)
+  int32_t n_kblocks;         // dK/dV kernel: ceil(kv_len / 128)
+  int32_t causal;
+  int32_t accumulate;
+  float c;                   // softmax_scale * log2(e), rounded to fp32
+  float scale;               // softmax_scale
+};
+
 hipError_t launch_prefill(const PrefillArgs& a, int block, bool out_f32, bool emit, hipStream_t s);
+// Pre-pass, dQ and dK/dV launches of the backward, in that order on s.
+hipError_t launch_backward(const BackwardArgs& a, bool out_f32, hipStream_t s);
 // Fused prefill with K/V gathered from paged pools (a.page_table etc. set).
 hipError_t launch_prefill_paged(const PrefillArgs& a, int block, bool out_f32, hipStream_t s);
 hipError_t launch_decode_items(const DecodeArgs& a, int block, bool out_f32, hipStream_t s);

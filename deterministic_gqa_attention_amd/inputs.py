@@ -26,7 +26,7 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-TID_Q, TID_K, TID_V, TID_LENS, TID_PAGES, TID_RELOC, TID_ARRIVAL = 1, 2, 3, 4, 5, 6, 7
+TID_Q, TID_K, TID_V, TID_LENS, TID_PAGES, TID_RELOC, TID_ARRIVAL, TID_DOUT = 1, 2, 3, 4, 5, 6, 7, 8
 
 
 # --------------------------------------------------------------------------- bf16
@@ -174,6 +174,15 @@ def prefill_inputs(cfg: PrefillConfig, *, B=None, S=None, seed_cfg=None):
                   rope_theta=cfg.rope_theta)
     v = draw_bf16(1000 * c + TID_V, (B, S, cfg.Hkv, cfg.D))
     return q, k, v
+
+
+def dout_inputs(cfg: PrefillConfig, *, B=None, S=None, seed_cfg=None):
+    """Upstream gradient dOut [B, S, Hq, D] (bf16 bit patterns) for the backward
+    of a prefill config: standard normals, like the other activations."""
+    B = cfg.B if B is None else B
+    S = cfg.S if S is None else S
+    c = cfg.cfg_id if seed_cfg is None else seed_cfg
+    return draw_bf16(1000 * c + TID_DOUT, (B, S, cfg.Hq, cfg.D))
 
 
 def arrival_shuffle(cfg_id: int, n: int) -> np.ndarray:

@@ -197,6 +197,36 @@ rla_status rla_attn_decode_paged(const rla_attn_params* p, const void* q, const 
 rla_status rla_merge_states(const rla_attn_params* p, const rla_partials* parts, void* out, float* lse,
                             void* hip_stream);
 
+/* Backward of (chunked) prefill: dQ, dK, dV of Out ("[WS2][Attention] H100
+ * validation and reproduction guide", sections "PR stack": the prefill and
+ * chunked-prefill backward leg; "Status" and "Acceptance": dQ, dK and dV
+ * bitwise equal across decompositions).  The queries are those of
+ * rla_attn_prefill_chunked: query i sits at position cache_len + i and attends
+ * keys [0, cache_len + q_rows) (causally when p->causal); full prefill is
+ * cache_len = 0, q_rows = s_max = seq_len.
+ * Inputs (device, bf16 unless noted): q, dout [batch][q_rows][Hq][128];
+ * k, v [batch][s_max][Hkv][128]; out [batch][q_rows][Hq][128], the forward
+ * output in p->out_dtype (bf16 or fp32); lse [batch][q_rows][Hq] fp32, the
+ * forward's natural-log LSE.  The gradient reaching LSE is taken as zero.
+ * Outputs (device, fp32): dq [batch][q_rows][Hq][128]; dk, dv
+ * [batch][s_max][Hkv][128], written for keys [0, cache_len + q_rows) only.
+ * accumulate = 0: dk/dv are overwritten.  accumulate = 1: this call's
+ * contributions are added to the fp32 values already in dk/dv (which the
+ * caller zero-fills before the first call): replaying the query rows as
+ * consecutive chunks whose cache_len are multiples of 64 gives dq, dk and dv
+ * bit for bit equal to one call over all rows.
+ * Every element is one fixed-order FP32 MFMA accumulation (dK/dV: query tiles
+ * of 64 rows in ascending order, q heads of the group in ascending order
+ * inside a tile; dQ: keys in ascending order), so results do not depend on
+ * the batch makeup or on scheduling.  P and dS are rounded to bf16 as MFMA
+ * operands; dS includes softmax_scale.  kv_block_size is not used.  Takes a
+ * per-row scratch (8 bytes per query row and head), stream-ordered, from the
+ * library's device memory pool. */
+rla_status rla_attn_backward(const rla_attn_params* p, const void* q, const void* k, const void* v,
+                             const void* out, const float* lse, const void* dout, int32_t batch,
+                             int32_t q_rows, int32_t cache_len, int32_t s_max, int32_t accumulate,
+                             float* dq, float* dk, float* dv, void* hip_stream);
+
 /* Workspace bytes rla_attn_decode_paged needs (0 on invalid arguments). */
 size_t rla_decode_workspace_bytes(const rla_attn_params* p, int32_t batch, int32_t max_context_len);
 

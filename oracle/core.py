@@ -50,7 +50,7 @@ def _load(path=None):
                                      P, i64, P, P]
     lib.orc_decode_paged.restype = i32
     lib.orc_attention_backward.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, i32, i64, i32, i64,
-                                           f64, P, P, P, P, P, P]
+                                           f64, P, i64, P, P, P, P, P, P]
     lib.orc_attention_backward.restype = i32
     _libs[path] = lib
     return lib
@@ -173,12 +173,14 @@ def decode_paged(q, k_pool, v_pool, page_table, ctx_lens, *, scale, seqs=None, l
 
 
 def attention_backward(q, k, v, dout, *, scale, causal=True, pos0=0, kv_len=None, mags=False,
-                       lib_path=None):
+                       rows=None, lib_path=None):
     """Exact FP64 gradient of attention's Out (see ``orc_attention_backward``).
 
     q, dout: uint16 [B, Sq, Hq, D]; k, v: uint16 [B, Skv, Hkv, D].
     Returns (dq [B, Sq, Hq, D], dk [B, Skv, Hkv, D], dv [B, Skv, Hkv, D]) in float64,
     followed by (mag_dq, mag_dk, mag_dv) of the same shapes when ``mags`` is set.
+    rows: optional ascending flat indices ``b * Sq + t``; only those rows are
+    taken (their dQ is complete, dK/dV hold only their terms, other dQ rows are 0).
     """
     q, k, v, dout = _u16(q, "q"), _u16(k, "k"), _u16(v, "v"), _u16(dout, "dout")
     B, Sq, Hq, D = q.shape
@@ -191,9 +193,12 @@ def attention_backward(q, k, v, dout, *, scale, causal=True, pos0=0, kv_len=None
     dv = np.empty(k.shape, np.float64)
     m = [np.empty(q.shape, np.float64), np.empty(k.shape, np.float64),
          np.empty(k.shape, np.float64)] if mags else [None, None, None]
+    rows_arr = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    n_rows = 0 if rows_arr is None else rows_arr.size
     rc = _load(lib_path).orc_attention_backward(
         _ptr(q), _ptr(k), _ptr(v), _ptr(dout), B, Sq, Skv, Hq, Hkv, D, int(pos0), int(bool(causal)),
-        kv_len, float(scale), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(m[0]), _ptr(m[1]), _ptr(m[2]))
+        kv_len, float(scale), _ptr(rows_arr), n_rows, _ptr(dq), _ptr(dk), _ptr(dv), _ptr(m[0]),
+        _ptr(m[1]), _ptr(m[2]))
     if rc != 0:
         raise ValueError(f"orc_attention_backward rejected its arguments (rc={rc})")
     return (dq, dk, dv, *m) if mags else (dq, dk, dv)

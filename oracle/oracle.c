@@ -323,16 +323,25 @@ int orc_decode_paged(const uint16_t* q, const uint16_t* k_pool, const uint16_t* 
  *
  * Layouts: q, dout [B][Sq][Hq][D]; k, v [B][Skv][Hkv][D] (bf16 bits);
  * dq and mag_dq [B][Sq][Hq][D], dk, dv, mag_dk, mag_dv [B][Skv][Hkv][D]
- * (double).  Query t sits at position pos0 + t.  Returns 0, or -1 on bad
- * arguments.
+ * (double).  Query t sits at position pos0 + t.
+ * rows: ascending flat indices b*Sq + t of the query rows to take (NULL = all
+ * rows).  dQ of the listed rows is complete; dK and dV then hold only the
+ * listed rows' terms (a sample, for checking dQ of a few rows of a large
+ * problem).  Returns 0, or -1 on bad arguments.
  */
 int orc_attention_backward(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                            const uint16_t* dout, int B, int Sq, int Skv, int Hq, int Hkv, int D,
                            int64_t pos0, int causal, int64_t kv_len, double scale,
+                           const int64_t* rows, int64_t n_rows,
                            double* dq, double* dk, double* dv,
                            double* mag_dq, double* mag_dk, double* mag_dv) {
     if (B <= 0 || Sq < 0 || Skv < 0 || Hq <= 0 || Hkv <= 0 || D <= 0) return -1;
     if (Hq % Hkv != 0 || kv_len > Skv || kv_len < 0) return -1;
+    if (rows != NULL) {
+        for (int64_t r = 0; r < n_rows; ++r) {
+            if (rows[r] < 0 || rows[r] >= (int64_t)B * Sq || (r > 0 && rows[r] <= rows[r - 1])) return -1;
+        }
+    }
     const int group = Hq / Hkv;
     int bad = 0;
     memset(dq, 0, sizeof(double) * (size_t)B * Sq * Hq * D);
@@ -359,8 +368,17 @@ int orc_attention_backward(const uint16_t* q, const uint16_t* k, const uint16_t*
             if (s == NULL || dp == NULL || adp == NULL) continue;
             const int64_t b = pair / Hkv;
             const int hk = (int)(pair % Hkv);
+            /* this batch row's span of the row list */
+            int64_t r_lo = 0, r_hi = Sq;
+            if (rows != NULL) {
+                r_lo = 0;
+                while (r_lo < n_rows && rows[r_lo] < b * Sq) ++r_lo;
+                r_hi = r_lo;
+                while (r_hi < n_rows && rows[r_hi] < (b + 1) * Sq) ++r_hi;
+            }
             for (int h = hk * group; h < (hk + 1) * group; ++h) {
-                for (int64_t t = 0; t < Sq; ++t) {
+                for (int64_t r = r_lo; r < r_hi; ++r) {
+                    const int64_t t = rows != NULL ? rows[r] - b * Sq : r;
                     const int64_t pos = pos0 + t;
                     int64_t hi = kv_len;
                     if (causal && hi > pos + 1) hi = pos + 1;

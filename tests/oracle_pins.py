@@ -370,6 +370,24 @@ def pin_backward_gqa_and_chunks(lib_path=None):
     _close(sv, dv, tol=1e-13, what="chunked dV sum")
 
 
+def pin_backward_row_subset(lib_path=None):
+    """dQ of a listed row subset equals those rows of the full call (bitwise);
+    dK/dV of a partition of the rows add up to the full dK/dV."""
+    B, S, Hq, Hkv, D = 2, 7, 4, 2, 8
+    q, k = _rand(481, (B, S, Hq, D)), _rand(482, (B, S, Hkv, D))
+    v, do = _rand(483, (B, S, Hkv, D)), _rand(484, (B, S, Hq, D))
+    dq, dk, dv = oracle.attention_backward(q, k, v, do, scale=0.3, lib_path=lib_path)
+    part = [0, 3, 4, 9, 13]
+    rest = [r for r in range(B * S) if r not in part]
+    aq, ak, av = oracle.attention_backward(q, k, v, do, scale=0.3, rows=part, lib_path=lib_path)
+    bq, bk, bv = oracle.attention_backward(q, k, v, do, scale=0.3, rows=rest, lib_path=lib_path)
+    flat = dq.reshape(B * S, Hq, D)
+    _bits_equal(aq.reshape(B * S, Hq, D)[part], flat[part], "subset dQ rows")
+    assert not aq.reshape(B * S, Hq, D)[rest].any(), "unlisted dQ rows must stay 0"
+    _close(ak + bk, dk, tol=1e-13, what="partitioned dK")
+    _close(av + bv, dv, tol=1e-13, what="partitioned dV")
+
+
 def pin_backward_magnitudes(lib_path=None):
     """The error-bound magnitudes dominate the gradients they bound (triangle
     inequality), and vanish exactly where the gradient has no term."""
@@ -388,4 +406,5 @@ ALL_PINS = [pin_brute_force, pin_single_key_row, pin_uniform_scores, pin_constan
             pin_two_key_closed_form, pin_merge_identity, pin_merge_permutation, pin_causality,
             pin_gqa_replication, pin_chunk_equals_full, pin_decode_equals_prefill_last_row,
             pin_backward_finite_differences, pin_backward_shift_invariances,
-            pin_backward_single_key, pin_backward_gqa_and_chunks, pin_backward_magnitudes]
+            pin_backward_single_key, pin_backward_gqa_and_chunks, pin_backward_row_subset,
+            pin_backward_magnitudes]

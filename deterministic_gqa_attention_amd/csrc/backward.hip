@@ -207,6 +207,7 @@ __global__ __launch_bounds__(kDqWaves * 64) void bwd_dq_kernel(const BackwardArg
     if (!sees) continue;
     const bool full = key0 + kQB <= kvl && (!a.causal || key0 + kQB - 1 <= a.pos0 + t0) && t_last == t0 + 31;
 
+    // S^T = K Q^T and dP^T = V dOut^T, fragments read one D-step ahead.
     f32x16 s[2], dp[2];
     {
       const RowReadsV kr(kreg);
@@ -216,37 +217,58 @@ __global__ __launch_bounds__(kDqWaves * 64) void bwd_dq_kernel(const BackwardArg
         s[kt] = f32x16{};
         dp[kt] = f32x16{};
       }
+      bf16x8 fa[2][4];
+      auto rd = [&](int ds, int slot) {
+        fa[slot][0] = kr.frag(0, ds);
+        fa[slot][1] = kr.frag(1, ds);
+        fa[slot][2] = vr.frag(0, ds);
+        fa[slot][3] = vr.frag(1, ds);
+      };
+      rd(0, 0);
 #pragma unroll
       for (int ds = 0; ds < kDSteps; ++ds) {
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-          s[kt] = mfma(kr.frag(kt, ds), qf[ds], s[kt]);
-          dp[kt] = mfma(vr.frag(kt, ds), of[ds], dp[kt]);
-        }
+        if (ds + 1 < kDSteps) rd(ds + 1, (ds + 1) & 1);
+        s[0] = mfma(fa[ds & 1][0], qf[ds], s[0]);
+        s[1] = mfma(fa[ds & 1][1], qf[ds], s[1]);
+        dp[0] = mfma(fa[ds & 1][2], of[ds], dp[0]);
+        dp[1] = mfma(fa[ds & 1][3], of[ds], dp[1]);
+        sched_fence();
       }
     }
-    // P and dS; key of register v of sub-tile kt: key0 + 32kt + 8(v/4) + 4half + v%4.
+    // P and dS (into s) of register v of key sub-tile kt, whose key is
+    // key0 + 32kt + 8(v/4) + 4half + v%4.
     const int room = limit - (key0 + 4 * half);
+    auto grad = [&](int kt, int v) {
+      const int off = kt * 32 + 8 * (v >> 2) + (v & 3);
+      const float p = hw_exp2(fmaf(s[kt][v], a.c, -lse2));
+      const float pm = (full || off <= room) ? p : 0.0f;
+      const float d = dp[kt][v] - delta;
+      const float g = pm * d;
+      s[kt][v] = g * a.scale;
+    };
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
+    for (int v = 0; v < 16; ++v) grad(0, v);
+    // dQ^T += K^T dS^T in 16 steps (key sub-tile kt, 16-key step st, dim tile
+    // dt), transposed K fragments read two steps ahead; the vector work of
+    // sub-tile 1 runs between the MFMAs of sub-tile 0.
+    {
+      const VReads<kQB> ktr(kreg);
+      bf16x8 fk[3];
+      auto rd = [&](int step, int slot) { fk[slot] = ktr.frag(step & 3, step >> 3, (step >> 2) & 1); };
+      rd(0, 0);
+      rd(1, 1);
+      bf16x8 bf;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int off = kt * 32 + 8 * (v >> 2) + (v & 3);
-        const float p = hw_exp2(fmaf(s[kt][v], a.c, -lse2));
-        const float pm = (full || off <= room) ? p : 0.0f;
-        const float d = dp[kt][v] - delta;
-        const float g = pm * d;
-        s[kt][v] = g * a.scale;  // s now holds dS
-      }
-    }
-    const VReads<kQB> ktr(kreg);
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        const bf16x8 bf = pack8(s[kt], st);
-#pragma unroll
-        for (int dt = 0; dt < kDTiles; ++dt) acc[dt] = mfma(ktr.frag(dt, kt, st), bf, acc[dt]);
+      for (int step = 0; step < 16; ++step) {
+        if (step + 2 < 16) rd(step + 2, (step + 2) % 3);
+        const int kt = step >> 3, st = (step >> 2) & 1, dt = step & 3;
+        if (dt == 0) bf = pack8(s[kt], st);
+        acc[dt] = mfma(fk[step % 3], bf, acc[dt]);
+        if (step < 8) {
+          grad(1, 2 * step);
+          grad(1, 2 * step + 1);
+        }
+        sched_fence();
       }
     }
   }
@@ -373,11 +395,28 @@ void bwd_dkdv_kernel(const BackwardArgs a) {
     const int64_t pos_last = a.pos0 + min(a.Sq, tr0 + kQT) - 1;
     const bool sees = kw0 < kvl && (!a.causal || kw0 <= pos_last);
     if (!sees) continue;
-    const bool full = kw0 + 31 < kvl && rows_left >= kQT && (!a.causal || kw0 + 31 <= a.pos0 + tr0);
     const char* base = stage + (i & 1) * KvStage::kBytes;
     const char* qreg = base + KvStage::kQ;
     const char* oreg = base + KvStage::kO;
 
+    // LSE*log2e and Delta of the lane's rows: register v of row tile qt is
+    // row r = 32qt + 8(v/4) + 4half + v%4 of the tile.
+    f32x4 Lr[2][4], Dr[2][4];
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r0 = 32 * qt + 8 * j + 4 * half;
+        Lr[qt][j] = *reinterpret_cast<const f32x4*>(base + KvStage::kL + r0 * 4);
+        Dr[qt][j] = *reinterpret_cast<const f32x4*>(base + KvStage::kD + r0 * 4);
+      }
+    }
+    // Rows r of the tile that see this lane's key: rmin <= r < rmax (row in
+    // range, key in range, and causally key <= pos0 + tr0 + r).
+    const int rmax = key_ok ? rows_left : 0;
+    const int rmin = a.causal ? max(0, key - static_cast<int>(a.pos0 + tr0)) : 0;
+
+    // S = Q K^T and dP = dOut V^T, fragments read one D-step ahead.
     f32x16 s[2], dp[2];
     {
       const RowReadsV qr(qreg);
@@ -387,53 +426,69 @@ void bwd_dkdv_kernel(const BackwardArgs a) {
         s[qt] = f32x16{};
         dp[qt] = f32x16{};
       }
+      bf16x8 fa[2][4];
+      auto rd = [&](int ds, int slot) {
+        fa[slot][0] = qr.frag(0, ds);
+        fa[slot][1] = qr.frag(1, ds);
+        fa[slot][2] = orr.frag(0, ds);
+        fa[slot][3] = orr.frag(1, ds);
+      };
+      rd(0, 0);
 #pragma unroll
       for (int ds = 0; ds < kDSteps; ++ds) {
-#pragma unroll
-        for (int qt = 0; qt < 2; ++qt) {
-          s[qt] = mfma(qr.frag(qt, ds), kf[ds], s[qt]);
-          dp[qt] = mfma(orr.frag(qt, ds), vf[ds], dp[qt]);
-        }
+        if (ds + 1 < kDSteps) rd(ds + 1, (ds + 1) & 1);
+        s[0] = mfma(fa[ds & 1][0], kf[ds], s[0]);
+        s[1] = mfma(fa[ds & 1][1], kf[ds], s[1]);
+        dp[0] = mfma(fa[ds & 1][2], vf[ds], dp[0]);
+        dp[1] = mfma(fa[ds & 1][3], vf[ds], dp[1]);
+        sched_fence();
       }
     }
-    // Register v of row tile qt is row r = 32qt + 8(v/4) + 4half + v%4 of the
-    // tile; the lane's key is `key`.  Visible: row in range, key in range,
-    // and (causal) key <= pos0 + tr0 + r.
-    const int room = static_cast<int>(a.pos0 + tr0) - key;  // key <= pos0 + tr0 + r  <=>  r + room >= 0
+    // P (into s) and dS (into dp) of register v of row tile qt.
+    auto grad = [&](int qt, int v) {
+      const int j = v >> 2;
+      const int e = v & 3;
+      const int r = 32 * qt + 8 * j + 4 * half + e;
+      const bool vis = (r >= rmin) & (r < rmax);
+      const float p = hw_exp2(fmaf(s[qt][v], c, -Lr[qt][j][e]));
+      const float pm = vis ? p : 0.0f;
+      const float d = dp[qt][v] - Dr[qt][j][e];
+      const float g = pm * d;
+      s[qt][v] = pm;
+      dp[qt][v] = g * scale;
+    };
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
+    for (int v = 0; v < 16; ++v) grad(0, v);
+    // dV^T += dOut^T P and dK^T += Q^T dS in 16 steps (row tile qt, 16-row
+    // step st, dim tile dt), transposed fragments read two steps ahead; the
+    // vector work of row tile 1 runs between the MFMAs of row tile 0.
+    {
+      const VReads<kQT> otr(oreg);
+      const VReads<kQT> qtr(qreg);
+      bf16x8 fo[3], fq[3];
+      auto rd = [&](int step, int slot) {
+        const int qt = step >> 3, st = (step >> 2) & 1, dt = step & 3;
+        fo[slot] = otr.frag(dt, qt, st);
+        fq[slot] = qtr.frag(dt, qt, st);
+      };
+      rd(0, 0);
+      rd(1, 1);
+      bf16x8 pb, db;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int r0 = 32 * qt + 8 * j + 4 * half;
-        const f32x4 L = *reinterpret_cast<const f32x4*>(base + KvStage::kL + r0 * 4);
-        const f32x4 Dl = *reinterpret_cast<const f32x4*>(base + KvStage::kD + r0 * 4);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int v = 4 * j + e;
-          const int r = r0 + e;
-          const bool vis = full || (key_ok && r < rows_left && (!a.causal || r + room >= 0));
-          const float p = hw_exp2(fmaf(s[qt][v], c, -L[e]));
-          const float pm = vis ? p : 0.0f;
-          const float d = dp[qt][v] - Dl[e];
-          const float g = pm * d;
-          s[qt][v] = pm;
-          dp[qt][v] = g * scale;  // dp now holds dS
+      for (int step = 0; step < 16; ++step) {
+        if (step + 2 < 16) rd(step + 2, (step + 2) % 3);
+        const int qt = step >> 3, st = (step >> 2) & 1, dt = step & 3;
+        if (dt == 0) {
+          pb = pack8(s[qt], st);
+          db = pack8(dp[qt], st);
         }
-      }
-    }
-    const VReads<kQT> otr(oreg);
-    const VReads<kQT> qtr(qreg);
-#pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        const bf16x8 pb = pack8(s[qt], st);
-        const bf16x8 db = pack8(dp[qt], st);
-#pragma unroll
-        for (int dt = 0; dt < kDTiles; ++dt) {
-          dv[dt] = mfma(otr.frag(dt, qt, st), pb, dv[dt]);
-          dk[dt] = mfma(qtr.frag(dt, qt, st), db, dk[dt]);
+        dv[dt] = mfma(fo[step % 3], pb, dv[dt]);
+        dk[dt] = mfma(fq[step % 3], db, dk[dt]);
+        if (step < 8) {
+          grad(1, 2 * step);
+          grad(1, 2 * step + 1);
         }
+        sched_fence();
       }
     }
   }

@@ -75,43 +75,51 @@ __device__ __forceinline__ bf16x8 pack8(const f32x16& x, int s) {
 
 // ------------------------------------------------------------- pre-pass --
 
-// One wave per (b, h, t) with t < Sq_pad: lane l takes dims 2l, 2l+1.
+// 16 lanes per (b, h, t) row, t < Sq_pad (four rows per wave): lane l of the
+// row takes dims 8l..8l+7; the eight products are summed in a fixed tree,
+// then the 16 lanes' sums by a butterfly.
 template <bool OUT_F32>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(const BackwardArgs a) {
-  const int wave = threadIdx.x >> 6;
-  const int lane = threadIdx.x & 63;
-  const int64_t item = static_cast<int64_t>(blockIdx.x) * 4 + wave;
+  const int sub = threadIdx.x & 15;
+  const int64_t item = static_cast<int64_t>(blockIdx.x) * 16 + (threadIdx.x >> 4);
   const int64_t total = static_cast<int64_t>(a.B) * a.Hq * a.Sq_pad;
-  if (item >= total) return;
-  const int t = static_cast<int>(item % a.Sq_pad);
-  const int64_t bh = item / a.Sq_pad;
+  const bool live = item < total;
+  const int64_t it = live ? item : 0;
+  const int t = static_cast<int>(it % a.Sq_pad);
+  const int64_t bh = it / a.Sq_pad;
   const int h = static_cast<int>(bh % a.Hq);
   const int b = static_cast<int>(bh / a.Hq);
   float x = 0.0f;
   float lse2 = 0.0f;
-  if (t < a.Sq) {
-    const int64_t e = static_cast<int64_t>(b) * a.q_bstride + (static_cast<int64_t>(t) * a.Hq + h) * kHeadDim + 2 * lane;
-    const uint32_t gw = *reinterpret_cast<const uint32_t*>(a.dout + e);
-    float o0, o1;
+  if (live && t < a.Sq) {
+    const int64_t e = static_cast<int64_t>(b) * a.q_bstride + (static_cast<int64_t>(t) * a.Hq + h) * kHeadDim + 8 * sub;
+    const u32x4 gw = *reinterpret_cast<const u32x4*>(a.dout + e);
+    float o[8];
     if constexpr (OUT_F32) {
-      const float2 o = *reinterpret_cast<const float2*>(static_cast<const float*>(a.out) + e);
-      o0 = o.x;
-      o1 = o.y;
+      const f32x4 o0 = *reinterpret_cast<const f32x4*>(static_cast<const float*>(a.out) + e);
+      const f32x4 o1 = *reinterpret_cast<const f32x4*>(static_cast<const float*>(a.out) + e + 4);
+      for (int i = 0; i < 4; ++i) {
+        o[i] = o0[i];
+        o[4 + i] = o1[i];
+      }
     } else {
-      const uint32_t ow = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(a.out) + e);
-      o0 = bf16_lo_to_f32(ow);
-      o1 = bf16_hi_to_f32(ow);
+      const u32x4 ow = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.out) + e);
+      for (int i = 0; i < 4; ++i) {
+        o[2 * i] = bf16_lo_to_f32(ow[i]);
+        o[2 * i + 1] = bf16_hi_to_f32(ow[i]);
+      }
     }
-    const float p0 = bf16_lo_to_f32(gw) * o0;
-    const float p1 = bf16_hi_to_f32(gw) * o1;
-    x = p0 + p1;
+    float p[8];
+    for (int i = 0; i < 4; ++i) {
+      p[2 * i] = bf16_lo_to_f32(gw[i]) * o[2 * i];
+      p[2 * i + 1] = bf16_hi_to_f32(gw[i]) * o[2 * i + 1];
+    }
+    x = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
     lse2 = a.lse[(static_cast<int64_t>(b) * a.Sq + t) * a.Hq + h] * kLog2e;
   }
-  // Butterfly: lanes i and i^m add the same two values (in swapped order,
-  // which IEEE addition does not see), so every lane ends with the same sum.
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) x = x + __shfl_xor(x, m, 64);
-  if (lane == 0) {
+  for (int m = 8; m >= 1; m >>= 1) x = x + __shfl_xor(x, m, 64);
+  if (live && sub == 0) {
     float* row = a.ws + bh * 2 * a.Sq_pad;
     row[t] = lse2;
     row[a.Sq_pad + t] = x;
@@ -426,7 +434,7 @@ void bwd_dkdv_kernel(const BackwardArgs a) {
         s[qt] = f32x16{};
         dp[qt] = f32x16{};
       }
-      bf16x8 fa[2][4];
+      bf16x8 fa[3][4];
       auto rd = [&](int ds, int slot) {
         fa[slot][0] = qr.frag(0, ds);
         fa[slot][1] = qr.frag(1, ds);
@@ -434,13 +442,14 @@ void bwd_dkdv_kernel(const BackwardArgs a) {
         fa[slot][3] = orr.frag(1, ds);
       };
       rd(0, 0);
+      rd(1, 1);
 #pragma unroll
       for (int ds = 0; ds < kDSteps; ++ds) {
-        if (ds + 1 < kDSteps) rd(ds + 1, (ds + 1) & 1);
-        s[0] = mfma(fa[ds & 1][0], kf[ds], s[0]);
-        s[1] = mfma(fa[ds & 1][1], kf[ds], s[1]);
-        dp[0] = mfma(fa[ds & 1][2], vf[ds], dp[0]);
-        dp[1] = mfma(fa[ds & 1][3], vf[ds], dp[1]);
+        if (ds + 2 < kDSteps) rd(ds + 2, (ds + 2) % 3);
+        s[0] = mfma(fa[ds % 3][0], kf[ds], s[0]);
+        s[1] = mfma(fa[ds % 3][1], kf[ds], s[1]);
+        dp[0] = mfma(fa[ds % 3][2], vf[ds], dp[0]);
+        dp[1] = mfma(fa[ds % 3][3], vf[ds], dp[1]);
         sched_fence();
       }
     }
@@ -465,7 +474,7 @@ void bwd_dkdv_kernel(const BackwardArgs a) {
     {
       const VReads<kQT> otr(oreg);
       const VReads<kQT> qtr(qreg);
-      bf16x8 fo[3], fq[3];
+      bf16x8 fo[4], fq[4];
       auto rd = [&](int step, int slot) {
         const int qt = step >> 3, st = (step >> 2) & 1, dt = step & 3;
         fo[slot] = otr.frag(dt, qt, st);
@@ -473,17 +482,18 @@ void bwd_dkdv_kernel(const BackwardArgs a) {
       };
       rd(0, 0);
       rd(1, 1);
+      rd(2, 2);
       bf16x8 pb, db;
 #pragma unroll
       for (int step = 0; step < 16; ++step) {
-        if (step + 2 < 16) rd(step + 2, (step + 2) % 3);
+        if (step + 3 < 16) rd(step + 3, (step + 3) % 4);
         const int qt = step >> 3, st = (step >> 2) & 1, dt = step & 3;
         if (dt == 0) {
           pb = pack8(s[qt], st);
           db = pack8(dp[qt], st);
         }
-        dv[dt] = mfma(fo[step % 3], pb, dv[dt]);
-        dk[dt] = mfma(fq[step % 3], db, dk[dt]);
+        dv[dt] = mfma(fo[step % 4], pb, dv[dt]);
+        dk[dt] = mfma(fq[step % 4], db, dk[dt]);
         if (step < 8) {
           grad(1, 2 * step);
           grad(1, 2 * step + 1);
@@ -511,7 +521,7 @@ void bwd_dkdv_kernel(const BackwardArgs a) {
 hipError_t launch_backward(const BackwardArgs& a, bool out_f32, hipStream_t s) {
   // pre-pass
   const int64_t rows = static_cast<int64_t>(a.B) * a.Hq * a.Sq_pad;
-  const int64_t g0 = (rows + 3) / 4;
+  const int64_t g0 = (rows + 15) / 16;
   if (g0 <= 0 || g0 > 0x7fffffff) return hipErrorInvalidConfiguration;
   if (out_f32) {
     hipLaunchKernelGGL((bwd_prep_kernel<true>), dim3(static_cast<unsigned>(g0)), dim3(256), 0, s, a);

@@ -297,7 +297,13 @@ struct VReads {
   const char* reg;
   int ref;
   int a[kDTiles][2];
-  __device__ __forceinline__ explicit VReads(const char* vreg) : reg(vreg), ref(lds_address(vreg)) {
+  __device__ __forceinline__ explicit VReads(const char* vreg) { init(vreg); }
+  __device__ __forceinline__ VReads() {}
+  // Bind to a region (at this point of the program, so the address registers
+  // live from here on).
+  __device__ __forceinline__ void init(const char* vreg) {
+    reg = vreg;
+    ref = lds_address(vreg);
     using L = TileLayout<BK>;
     const int lane = threadIdx.x & 63;
     const int i = lane & 15;

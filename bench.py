@@ -46,7 +46,10 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (published)
 PROFILES = os.path.join(ROOT, "profiles")
 PREFILL_PROFILE = os.path.join(PROFILES, "prefill_kernel_b4_s4096.md")
 DECODE_PROFILE = os.path.join(PROFILES, "decode_paged_64seq.md")
+BACKWARD_PROFILE = os.path.join(PROFILES, "backward_b4_s4096.md")
 TRACE_CMD = {
+    "backward": "rocprofv3 --kernel-trace --stats -d gpurun_out/prof_backward -o run --output-format csv -- "
+                "python3 bench.py --only backward --steps 10",
     "prefill": "rocprofv3 --kernel-trace --stats -d gpurun_out/prof_prefill -o run --output-format csv -- "
                "python3 bench.py --only prefill --steps 20 --warmup 3",
     "decode": "rocprofv3 --kernel-trace --stats -d gpurun_out/prof_decode -o run --output-format csv -- "
@@ -54,6 +57,8 @@ TRACE_CMD = {
 }
 PMC_CMD = ("rocprofv3 --pmc {c} -d gpurun_out/pmc_{c}_{m} -o run --output-format csv -- "
            "python3 bench.py --only {m} --steps 2 --warmup 1 --decode-steps 2")
+PMC_CMD_BACKWARD = ("rocprofv3 --pmc {c} -d gpurun_out/pmc_{c}_backward -o run --output-format csv -- "
+                    "python3 bench.py --only backward --steps 2")
 
 
 def log(msg):
@@ -570,6 +575,83 @@ def summarize_profiles(d):
     with open(DECODE_PROFILE, "w") as f:
         f.write("\n".join(lines))
     print(f"wrote {PREFILL_PROFILE} and {DECODE_PROFILE}")
+    if os.path.isdir(os.path.join(d, "prof_backward")):
+        summarize_backward(d, f_fetch, f_write, header, src)
+
+
+def summarize_backward(d, f_fetch, f_write, header, src):
+    """profiles/backward_b4_s4096.md from the backward kernel trace and counters."""
+    cfg = gen.CFG2
+    rows = _read_csv(os.path.join(d, "prof_backward", "run_kernel_stats.csv"))
+    kern = [(r["Name"], int(r["Calls"]), float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+             float(r["MaxNs"]) / 1e3) for r in rows if "bwd_" in r["Name"]]
+    order = {"bwd_prep": 0, "bwd_dq": 1, "bwd_dkdv": 2}
+    kern.sort(key=lambda r: min(v for k, v in order.items() if k in r[0]))
+    fwd = cfg.flops()
+    alg = 2.5 * fwd
+    executed = {"bwd_prep": 0.0, "bwd_dq": 1.5 * fwd, "bwd_dkdv": 2.0 * fwd}
+    B, S, Hq, Hkv, D = cfg.B, cfg.S, cfg.Hq, cfg.Hkv, cfg.D
+    alg_bytes = B * S * (3 * Hq + 2 * Hkv) * D * 2 + B * S * Hq * 4 + B * S * (Hq + 2 * Hkv) * D * 4
+    total_us = sum(r[2] for r in kern)
+
+    def counter(c, part):
+        vals = []
+        for r in _read_csv(os.path.join(d, f"pmc_{c}_backward", "run_counter_collection.csv")):
+            if part in r["Kernel_Name"] and r["Counter_Name"] == c:
+                vals.append(float(r["Counter_Value"]))
+        return sum(vals) / max(len(vals), 1), len(vals)
+
+    lines = [
+        "# Backward (dQ, dK, dV), causal B=4 S=4096 Hq=32 Hkv=8 D=128, bf16 in, fp32 gradients",
+        "",
+        "Kernel trace (three launches per backward call: pre-pass, dQ, dK/dV):",
+        "",
+        "    " + TRACE_CMD["backward"],
+        "",
+        "| kernel | calls | avg us | min us | max us | MFMA work executed (flop) | TFLOP/s executed at avg |",
+        "|---|---|---|---|---|---|---|",
+    ]
+    for name, calls, avg, mn, mx in kern:
+        ex = next(v for k, v in executed.items() if k in name)
+        rate = f"{ex / (avg * 1e-6) / 1e12:.1f}" if ex else "-"
+        lines.append(f"| `{name}` | {calls} | {avg:.1f} | {mn:.1f} | {mx:.1f} | {ex:.4e} | {rate} |")
+    lines += [
+        "",
+        f"Sum of averages {total_us:.1f} us.  Algorithmic work of one backward: {alg:.6e} flop (the five products "
+        "QK^T, dOut V^T, P^T dOut, dS^T Q, dS K over the unmasked pairs, 2.5x the forward's "
+        f"{fwd:.6e}) -> {alg / (total_us * 1e-6) / 1e12:.1f} TFLOP/s "
+        f"({alg / (total_us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS:.4f} of 2500).  The dQ kernel recomputes QK^T and "
+        "dOut V^T (no atomics, no dS in HBM), so the MFMA work executed is 3.5x the forward's.",
+        "",
+        f"Algorithmic HBM bytes: {alg_bytes} (Q, K, V, Out, dOut bf16 and LSE in; dQ, dK, dV fp32 out).",
+        "",
+        "HBM counters, one run per counter:",
+        "",
+    ] + ["    " + PMC_CMD_BACKWARD.format(c=c) for c in ("FETCH_SIZE", "WRITE_SIZE")] + [
+        "",
+        header,
+        "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | fetch bytes | write bytes |",
+        "|---|---|---|---|---|",
+    ]
+    tot = 0
+    for part in ("bwd_prep", "bwd_dq", "bwd_dkdv"):
+        fk, _ = counter("FETCH_SIZE", part)
+        wk, _ = counter("WRITE_SIZE", part)
+        fb, wb = int(round(fk * 1024 * f_fetch)), int(round(wk * 1024 * f_write))
+        tot += fb + wb
+        lines.append(f"| {part} | {fk:.1f} | {wk:.1f} | {fb} | {wb} |")
+    lines += [
+        "",
+        f"traffic bytes per backward: `{tot}` ({tot / alg_bytes:.2f} x algorithmic; the dK/dV walk re-reads the "
+        "Q and dOut tiles of its kv head once per 128-key block, and the dQ walk the K/V blocks once per "
+        "64-row tile)",
+        "",
+        f"kernel source sha256: `{src}`",
+        "",
+    ]
+    with open(BACKWARD_PROFILE, "w") as f:
+        f.write("\n".join(lines))
+    print(f"wrote {BACKWARD_PROFILE}")
 
 
 if __name__ == "__main__":

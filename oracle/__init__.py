@@ -12,7 +12,7 @@ Two independent implementations live here:
   scores without any max subtraction.  It exists only to pin the C oracle.
 """
 from .core import (ORACLE_LIB, attention, attention_backward, block_states, build, decode_paged,
-                   merge, oracle_threads)
+                   lm_head_logprobs, merge, oracle_threads)
 
 __all__ = ["ORACLE_LIB", "attention", "attention_backward", "block_states", "build",
-           "decode_paged", "merge", "oracle_threads"]
+           "decode_paged", "lm_head_logprobs", "merge", "oracle_threads"]

@@ -52,6 +52,8 @@ def _load(path=None):
     lib.orc_attention_backward.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, i32, i64, i32, i64,
                                            f64, P, i64, P, P, P, P, P, P]
     lib.orc_attention_backward.restype = i32
+    lib.orc_lm_head_logprobs.argtypes = [P, P, P, P, i32, i32, i32, P, P, P]
+    lib.orc_lm_head_logprobs.restype = i32
     _libs[path] = lib
     return lib
 
@@ -202,3 +204,32 @@ def attention_backward(q, k, v, dout, *, scale, causal=True, pos0=0, kv_len=None
     if rc != 0:
         raise ValueError(f"orc_attention_backward rejected its arguments (rc={rc})")
     return (dq, dk, dv, *m) if mags else (dq, dk, dv)
+
+
+def lm_head_logprobs(x, w, tokens, *, mags=False, lib_path=None):
+    """Selected log-probabilities through an FP32 lm_head (see ``orc_lm_head_logprobs``).
+
+    x: [T, H] as uint16 bf16 bits or float32; w: float32 [V, H]; tokens: int32 [T].
+    Returns (logp [T], logZ [T]) in float64, plus mag [T] when ``mags`` is set.
+    """
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    tokens = np.ascontiguousarray(tokens, dtype=np.int32)
+    x = np.ascontiguousarray(x)
+    if x.dtype == np.uint16:
+        xb, xf = x, None
+    elif x.dtype == np.float32:
+        xb, xf = None, x
+    else:
+        raise TypeError("x must be bf16 bits (uint16) or float32")
+    T, H = x.shape
+    V, Hw = w.shape
+    if Hw != H or tokens.shape != (T,):
+        raise ValueError("shape mismatch between x, w and tokens")
+    logp = np.empty(T, np.float64)
+    logz = np.empty(T, np.float64)
+    mag = np.empty(T, np.float64) if mags else None
+    rc = _load(lib_path).orc_lm_head_logprobs(_ptr(xb), _ptr(xf), _ptr(w), _ptr(tokens), T, H, V, _ptr(logp),
+                                              _ptr(logz), _ptr(mag))
+    if rc != 0:
+        raise ValueError(f"orc_lm_head_logprobs rejected its arguments (rc={rc})")
+    return (logp, logz, mag) if mags else (logp, logz)

@@ -437,3 +437,66 @@ int orc_attention_backward(const uint16_t* q, const uint16_t* k, const uint16_t*
     }
     return bad ? -1 : 0;
 }
+
+/*
+ * Selected log-probability through a synthetic FP32 lm_head ([P1] "Scope":
+ * both attention outputs are projected through the same deterministic
+ * synthetic FP32 lm_head and the active-token selected log-prob drift is
+ * reported; [P3] "Status": decode/prefill dlogp max abs 0.0).
+ *
+ * Definition, per active token t with attention output x_t (the Out row of
+ * the token, all q heads side by side: H = Hq * D values) and token id y_t:
+ *   z_tv   = sum_h x_th * W_vh              (logits, v < V)
+ *   logZ_t = ln sum_v exp(z_tv)
+ *   logp_t = z_{t, y_t} - logZ_t
+ * x is given as bf16 bits (x_f32 == NULL) or as fp32 (x_bf16 == NULL), W as
+ * fp32 [V][H]; everything is widened exactly and evaluated in double.
+ * Optional mag [T] (may be NULL): max_v sum_h |x_th| |W_vh|, the magnitude a
+ * bound on a finite-precision evaluation of the logits scales.
+ * Returns 0, or -1 on bad arguments (including a token id outside [0, V)).
+ */
+int orc_lm_head_logprobs(const uint16_t* x_bf16, const float* x_f32, const float* w, const int32_t* tokens,
+                         int T, int H, int V, double* logp, double* logz, double* mag) {
+    if (T < 0 || H <= 0 || V <= 0 || w == NULL || tokens == NULL || logp == NULL) return -1;
+    if ((x_bf16 == NULL) == (x_f32 == NULL)) return -1;
+    for (int t = 0; t < T; ++t) {
+        if (tokens[t] < 0 || tokens[t] >= V) return -1;
+    }
+    int bad = 0;
+#pragma omp parallel
+    {
+        double* z = (double*)malloc(sizeof(double) * (size_t)V);
+        double* xs = (double*)malloc(sizeof(double) * (size_t)H);
+        if (z == NULL || xs == NULL) {
+#pragma omp atomic write
+            bad = 1;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (int t = 0; t < T; ++t) {
+            if (z == NULL || xs == NULL) continue;
+            for (int h = 0; h < H; ++h)
+                xs[h] = x_bf16 ? bf16_to_double(x_bf16[(int64_t)t * H + h]) : (double)x_f32[(int64_t)t * H + h];
+            double m = -INFINITY, big = 0.0;
+            for (int v = 0; v < V; ++v) {
+                const float* row = w + (int64_t)v * H;
+                double acc = 0.0, aabs = 0.0;
+                for (int h = 0; h < H; ++h) {
+                    acc += xs[h] * (double)row[h];
+                    aabs += fabs(xs[h]) * fabs((double)row[h]);
+                }
+                z[v] = acc;
+                if (acc > m) m = acc;
+                if (aabs > big) big = aabs;
+            }
+            double sum = 0.0;
+            for (int v = 0; v < V; ++v) sum += exp(z[v] - m);
+            const double lz = m + log(sum);
+            logp[t] = z[tokens[t]] - lz;
+            if (logz) logz[t] = lz;
+            if (mag) mag[t] = big;
+        }
+        free(z);
+        free(xs);
+    }
+    return bad ? -1 : 0;
+}

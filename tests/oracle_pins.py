@@ -402,9 +402,70 @@ def pin_backward_magnitudes(lib_path=None):
     assert mq.min() > 0
 
 
+# -------------------------------------------------------------- lm_head pins
+
+
+def _lm_inputs(seed, T, H, V, xscale=1.0):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    x = gen.f64_to_bf16_bits(rng.standard_normal((T, H)) * xscale)
+    w = (rng.standard_normal((V, H)) / np.sqrt(H)).astype(np.float32)
+    tok = rng.integers(0, V, T).astype(np.int32)
+    return x, w, tok
+
+
+def pin_lm_head_brute_force(lib_path=None):
+    """Selected log-probs equal a numpy brute force (float64 matmul, plain
+    exp-sum without max subtraction) for bf16 and fp32 inputs."""
+    for n, (T, H, V) in enumerate(((5, 16, 7), (3, 24, 40), (1, 8, 1))):
+        x, w, tok = _lm_inputs(500 + n, T, H, V)
+        for xin in (x, brute.bf16_bits_to_f64(x).astype(np.float32)):
+            lp, lz = oracle.lm_head_logprobs(xin, w, tok, lib_path=lib_path)
+            z = brute.bf16_bits_to_f64(x) @ w.astype(np.float64).T
+            blz = np.log(np.exp(z).sum(axis=1))
+            _close(lz, blz, tol=1e-12, what=f"lm_head logZ case {n}")
+            _close(lp, z[np.arange(T), tok] - blz, tol=1e-12, what=f"lm_head logp case {n}")
+
+
+def pin_lm_head_closed_forms(lib_path=None):
+    """W = 0 gives logp = -ln V exactly; a common vector added to every row of W
+    changes nothing; the probabilities of all tokens sum to 1; V = 2 is a
+    log-sigmoid of the logit difference."""
+    T, H, V = 4, 32, 9
+    x, w, tok = _lm_inputs(511, T, H, V)
+    lp, _ = oracle.lm_head_logprobs(x, np.zeros_like(w), tok, lib_path=lib_path)
+    assert np.array_equal(lp, np.full(T, -np.log(V))), "W = 0 must give -ln V"
+    # rows and shift on a 2^-8 grid, so the shifted rows are exact in fp32
+    rng = np.random.Generator(np.random.PCG64(512))
+    wg = (np.round(rng.standard_normal((V, H)) * 64) / 256).astype(np.float32)
+    shift = (np.round(rng.standard_normal(H) * 64) / 256).astype(np.float32)
+    lp1, _ = oracle.lm_head_logprobs(x, wg, tok, lib_path=lib_path)
+    lp2, _ = oracle.lm_head_logprobs(x, wg + shift, tok, lib_path=lib_path)
+    _close(lp1, lp2, tol=1e-12, what="row shift")
+    total = np.zeros(T)
+    for v in range(V):
+        p, _ = oracle.lm_head_logprobs(x, w, np.full(T, v, np.int32), lib_path=lib_path)
+        total += np.exp(p)
+    _close(total, 1.0, tol=1e-12, what="probabilities sum to 1")
+    w2 = w[:2].copy()
+    lpa, _ = oracle.lm_head_logprobs(x, w2, np.zeros(T, np.int32), lib_path=lib_path)
+    xd = brute.bf16_bits_to_f64(x)
+    dz = xd @ (w2[1].astype(np.float64) - w2[0].astype(np.float64))
+    _close(lpa, -np.log1p(np.exp(dz)), tol=1e-12, what="V=2 log-sigmoid")
+
+
+def pin_lm_head_magnitude(lib_path=None):
+    """The magnitude dominates every |logit| of its token."""
+    T, H, V = 3, 16, 11
+    x, w, tok = _lm_inputs(521, T, H, V)
+    lp, lz, mag = oracle.lm_head_logprobs(x, w, tok, mags=True, lib_path=lib_path)
+    z = brute.bf16_bits_to_f64(x) @ w.astype(np.float64).T
+    assert (mag >= np.abs(z).max(axis=1) * (1 - 1e-12)).all()
+
+
 ALL_PINS = [pin_brute_force, pin_single_key_row, pin_uniform_scores, pin_constant_v,
             pin_two_key_closed_form, pin_merge_identity, pin_merge_permutation, pin_causality,
             pin_gqa_replication, pin_chunk_equals_full, pin_decode_equals_prefill_last_row,
             pin_backward_finite_differences, pin_backward_shift_invariances,
             pin_backward_single_key, pin_backward_gqa_and_chunks, pin_backward_row_subset,
-            pin_backward_magnitudes]
+            pin_backward_magnitudes, pin_lm_head_brute_force, pin_lm_head_closed_forms,
+            pin_lm_head_magnitude]

@@ -55,6 +55,12 @@ MUTATIONS = [
      "if (causal && hi > pos) hi = pos;", 1),
     ("bwd_wrong_group", "for (int h = hk * group; h < (hk + 1) * group; ++h) {",
      "for (int h = hk; h < Hq; h += Hkv) {", 0),
+    ("lm_logz_without_max", "const double lz = m + log(sum);", "const double lz = log(sum);", 0),
+    ("lm_wrong_token", "logp[t] = z[tokens[t]] - lz;", "logp[t] = z[(tokens[t] + 1) % V] - lz;", 0),
+    ("lm_sign", "logp[t] = z[tokens[t]] - lz;", "logp[t] = lz - z[tokens[t]];", 0),
+    ("lm_row_stride", "const float* row = w + (int64_t)v * H;", "const float* row = w + (int64_t)v;", 0),
+    ("lm_last_row_dropped", "for (int v = 0; v < V; ++v) sum += exp(z[v] - m);",
+     "for (int v = 0; v < V - 1; ++v) sum += exp(z[v] - m);", 0),
 ]
 
 

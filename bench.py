@@ -218,6 +218,40 @@ def backward_leg(api, cfg, qd, kd, vd, up, stream, steps):
             "workload": "backward of causal prefill B=4 S=4096 Hq=32 Hkv=8 D=128, bf16 in, fp32 dQ/dK/dV"}
 
 
+PEAK_FP32_TFLOPS = 157.3   # MI355X dense fp32 MFMA (published)
+
+
+def lm_head_leg(api, up, stream, reps=5):
+    """Selected log-probs of 64 active tokens (one per decode sequence, the
+    attention output of all 32 heads: H = 4096) through a synthetic FP32
+    lm_head over Qwen3-8B's 151936-token vocabulary: one pass over W (2.49 GB)
+    with 2*T*V*H flops of FP32 MFMA work."""
+    import torch
+    T, H, V = 64, 4096, gen.LM_VOCAB
+    log("generating the synthetic lm_head (151936 x 4096 fp32)")
+    w = torch.from_numpy(gen.lm_head_weights(V, H)).to(stream.device)
+    x = up(gen.draw_bf16(1000 * 4 + 11, (T, H)))
+    tok = torch.from_numpy(gen.lm_tokens(T, V)).to(stream.device)
+    api.lm_head_logprobs(x, w, tok)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        api.lm_head_logprobs(x, w, tok)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    flops = 2.0 * T * V * H
+    wbytes = V * H * 4
+    del w, x, tok
+    torch.cuda.empty_cache()
+    return {"ms": round(ms, 4), "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+            "frac_of_fp32_peak": round(flops / (ms * 1e-3) / 1e12 / PEAK_FP32_TFLOPS, 4),
+            "w_gbs": round(wbytes / (ms * 1e-3) / 1e9, 1),
+            "workload": "selected log-probs, 64 tokens x H=4096 bf16 through an fp32 lm_head of 151936 rows"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -228,7 +262,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-reported", action="store_true", help="skip the long-context and chunked-replay legs")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--only", choices=["prefill", "decode", "copy", "backward"], default=None,
+    ap.add_argument("--only", choices=["prefill", "decode", "copy", "backward", "lm_head"], default=None,
                     help="run one leg only (for profiler and counter runs)")
     ap.add_argument("--summarize", metavar="DIR", default=None,
                     help="write profiles/*.md from the rocprofv3 CSVs under DIR (no GPU work)")
@@ -276,6 +310,9 @@ def main():
     stream = torch.cuda.current_stream(dev)
     flops = cfg.flops()
 
+    if args.only == "lm_head":
+        print(json.dumps({"only": "lm_head", "lm_head": lm_head_leg(api, up, stream)}))
+        return
     if args.only == "backward":
         log("backward")
         print(json.dumps({"only": "backward", "backward": backward_leg(api, cfg, qd, kd, vd, up, stream,
@@ -332,6 +369,10 @@ def main():
         print(json.dumps({"only": "decode", "decode": decode}))
         return
     reported = None if args.no_reported else reported_legs(api, up, stream)
+    lm_head = None
+    if not args.no_reported:
+        lm_head = lm_head_leg(api, up, stream)
+        log(f"lm_head {lm_head['ms']:.3f} ms, {lm_head['tflops']:.1f} TFLOP/s fp32")
 
     line = {
         "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -345,6 +386,7 @@ def main():
                      "kernel_ms": round(kern_ms, 4)},
         "decode": decode,
         "backward": backward,
+        "lm_head_logprobs": lm_head,
         "invariance": {"batch_alone_vs_batch": drift_batch, "cp2_reversed_arrival": drift_cp},
         "reported": reported,
         "cpu_baseline": base,

@@ -20,8 +20,8 @@ RLA_MAX_PARTS = 512
 
 # Every function include/rla_attn.h declares.
 EXPORTS = ("rla_attn_prefill", "rla_attn_prefill_chunked", "rla_attn_prefill_paged", "rla_attn_decode_paged",
-           "rla_merge_states", "rla_attn_backward", "rla_decode_workspace_bytes", "rla_last_error",
-           "rla_core_id")
+           "rla_merge_states", "rla_attn_backward", "rla_lm_head_logprobs", "rla_decode_workspace_bytes",
+           "rla_last_error", "rla_core_id")
 
 
 class RlaParams(ctypes.Structure):
@@ -75,6 +75,8 @@ def load(path: str = LIB_PATH):
     lib.rla_attn_decode_paged.restype = ctypes.c_int
     lib.rla_attn_backward.argtypes = [pp, P, P, P, P, P, P, i32, i32, i32, i32, i32, P, P, P, P]
     lib.rla_attn_backward.restype = ctypes.c_int
+    lib.rla_lm_head_logprobs.argtypes = [P, i32, P, P, i32, i32, i32, P, P, P]
+    lib.rla_lm_head_logprobs.restype = ctypes.c_int
     lib.rla_merge_states.argtypes = [pp, ctypes.POINTER(RlaPartials), P, P, P]
     lib.rla_merge_states.restype = ctypes.c_int
     lib.rla_decode_workspace_bytes.argtypes = [pp, i32, i32]

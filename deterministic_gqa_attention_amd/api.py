@@ -16,7 +16,7 @@ from . import _lib
 from ._lib import RLAError, RlaParams, RlaPartials, RlaShard
 
 __all__ = ["RLAError", "core_id", "prefill", "prefill_chunked", "prefill_paged", "emit_partials",
-           "merge_states", "decode_paged", "decode_workspace_bytes", "backward", "params"]
+           "merge_states", "decode_paged", "decode_workspace_bytes", "backward", "lm_head_logprobs", "params"]
 
 _OUT_DT = {torch.bfloat16: _lib.RLA_DT_BF16, torch.float32: _lib.RLA_DT_FP32}
 _ORDER = {"global_block_index": _lib.RLA_ORDER_GLOBAL_BLOCK_INDEX, "arrival": _lib.RLA_ORDER_ARRIVAL}
@@ -149,6 +149,26 @@ def backward(q, k, v, out, lse, dout, *, cache_len=0, causal=True, scale=None, d
         _dev(dq, "dq", torch.float32, 4), _dev(dk, "dk", torch.float32, 4), _dev(dv, "dv", torch.float32, 4),
         _stream(q.device)))
     return dq, dk, dv
+
+
+def lm_head_logprobs(x, w, tokens):
+    """Selected log-probabilities through an FP32 lm_head.  x [T, H] (or any
+    [T, ...] contiguous tensor, flattened per token) bf16 or fp32; w [V, H]
+    fp32; tokens [T] int32.  Returns (logp [T], logz [T]) fp32."""
+    T = x.shape[0]
+    xf = x.reshape(T, -1)
+    V, H = w.shape
+    if xf.shape[1] != H:
+        raise ValueError(f"x has {xf.shape[1]} values per token, w has {H}")
+    if x.dtype not in _OUT_DT:
+        raise ValueError(f"x must be bf16 or fp32, got {x.dtype}")
+    logp = torch.empty(T, dtype=torch.float32, device=x.device)
+    logz = torch.empty(T, dtype=torch.float32, device=x.device)
+    lib = _lib.load()
+    _lib.check(lib.rla_lm_head_logprobs(
+        _dev(xf, "x", x.dtype, 2), _OUT_DT[x.dtype], _dev(w, "w", torch.float32, 2),
+        _dev(tokens, "tokens", torch.int32, 1), T, H, V, logp.data_ptr(), logz.data_ptr(), _stream(x.device)))
+    return logp, logz
 
 
 def emit_partials(q, k, v, kv_blocks, *, block, out_dtype=torch.bfloat16, causal=True, scale=None, q_begin=0,

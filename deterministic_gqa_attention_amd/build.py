@@ -21,7 +21,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "librla_attn.so")
-SOURCES = ["prefill.hip", "decode.hip", "fold.hip", "backward.hip", "api.cpp"]
+SOURCES = ["prefill.hip", "decode.hip", "fold.hip", "backward.hip", "lmhead.hip", "api.cpp"]
 ARCH = os.environ.get("RLA_OFFLOAD_ARCH", "gfx950")
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-ffp-contract=off", "-fno-fast-math", "-Wall",

@@ -484,6 +484,38 @@ rla_status rla_attn_backward(const rla_attn_params* p, const void* q, const void
   return hip_status(ef, "backward scratch free");
 }
 
+rla_status rla_lm_head_logprobs(const void* x, rla_dtype x_dtype, const float* w, const int32_t* tokens, int32_t T,
+                                int32_t H, int32_t V, float* logp, float* logz, void* hip_stream) {
+  if (x == nullptr || w == nullptr || tokens == nullptr || logp == nullptr)
+    return fail(RLA_ERR_NULL_POINTER, "a required pointer is NULL");
+  if (x_dtype != RLA_DT_BF16 && x_dtype != RLA_DT_FP32) return fail(RLA_ERR_UNSUPPORTED, "x_dtype=%d unsupported", x_dtype);
+  if (T < 1 || H < 8 || H % 8 != 0 || V < 1)
+    return fail(RLA_ERR_BAD_SHAPE, "need T>=1, H>=8 with H %% 8 == 0, V>=1 (got %d, %d, %d)", T, H, V);
+  rla::LmHeadArgs a;
+  std::memset(&a, 0, sizeof a);
+  a.x = x;
+  a.w = w;
+  a.tokens = tokens;
+  a.logp = logp;
+  a.logz = logz;
+  a.T = T;
+  a.H = H;
+  a.V = V;
+  a.n_vblocks = (V + 63) / 64;
+  a.n_tgroups = (T + 63) / 64;
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  const size_t bytes = (static_cast<size_t>(a.n_vblocks) * T * 2 + static_cast<size_t>(T)) * sizeof(float);
+  void* ws = nullptr;
+  hipError_t e = scratch_alloc(&ws, bytes, s);
+  if (e != hipSuccess) return hip_status(e, "lm_head scratch");
+  a.part = static_cast<float*>(ws);
+  a.zsel = a.part + static_cast<size_t>(a.n_vblocks) * T * 2;
+  e = rla::launch_lm_head(a, x_dtype == RLA_DT_FP32, s);
+  const hipError_t ef = hipFreeAsync(ws, s);
+  if (e != hipSuccess) return hip_status(e, "lm_head launch");
+  return hip_status(ef, "lm_head scratch free");
+}
+
 rla_status rla_merge_states(const rla_attn_params* p, const rla_partials* parts, void* out, float* lse,
                             void* hip_stream) {
   rla_status st = check_params(p, false, nullptr);

@@ -26,7 +26,8 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-TID_Q, TID_K, TID_V, TID_LENS, TID_PAGES, TID_RELOC, TID_ARRIVAL, TID_DOUT = 1, 2, 3, 4, 5, 6, 7, 8
+TID_Q, TID_K, TID_V, TID_LENS, TID_PAGES, TID_RELOC, TID_ARRIVAL, TID_DOUT, TID_LMW, TID_TOK = (
+    1, 2, 3, 4, 5, 6, 7, 8, 9, 10)
 
 
 # --------------------------------------------------------------------------- bf16
@@ -183,6 +184,24 @@ def dout_inputs(cfg: PrefillConfig, *, B=None, S=None, seed_cfg=None):
     S = cfg.S if S is None else S
     c = cfg.cfg_id if seed_cfg is None else seed_cfg
     return draw_bf16(1000 * c + TID_DOUT, (B, S, cfg.Hq, cfg.D))
+
+
+# Synthetic lm_head: Qwen3-8B's vocabulary over the attention output of all q
+# heads (H = Hq * D = 4096), W ~ N(0, 1/H) in fp32 so logits are O(|x|).
+LM_VOCAB = 151936
+
+
+def lm_head_weights(V: int, H: int, seed: int = 1000 * 4 + TID_LMW) -> np.ndarray:
+    """FP32 lm_head [V, H]: PCG64 standard normals drawn directly in float32,
+    scaled by 1/sqrt(H) (rounded once to fp32)."""
+    w = np.random.Generator(np.random.PCG64(seed)).standard_normal((V, H), dtype=np.float32)
+    w *= np.float32(1.0 / np.sqrt(H))
+    return w
+
+
+def lm_tokens(T: int, V: int, seed: int = 1000 * 4 + TID_TOK) -> np.ndarray:
+    """Active token ids [T], integer-uniform on [0, V)."""
+    return np.random.Generator(np.random.PCG64(seed)).integers(0, V, T).astype(np.int32)
 
 
 def arrival_shuffle(cfg_id: int, n: int) -> np.ndarray:

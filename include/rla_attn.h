@@ -227,6 +227,24 @@ rla_status rla_attn_backward(const rla_attn_params* p, const void* q, const void
                              int32_t q_rows, int32_t cache_len, int32_t s_max, int32_t accumulate,
                              float* dq, float* dk, float* dv, void* hip_stream);
 
+/* Selected log-probability through an FP32 lm_head ("WS2 Attention PR5 Drift
+ * Benchmark", section "Scope": both attention outputs of a drift comparison go
+ * through the same deterministic synthetic FP32 lm_head and the active
+ * tokens' selected log-probs are compared; "[WS2][Attention] H100 validation
+ * and reproduction guide", section "Status": decode/prefill dlogp max abs 0.0).
+ * For token t: z_tv = sum_h x[t][h] * w[v][h] (FP32 MFMA accumulation in a
+ * fixed order over h), logz[t] = ln sum_v exp(z_tv) (per-64-row block max and
+ * sum, folded in ascending block order), logp[t] = z_{t,tokens[t]} - logz[t].
+ * x [T][H] device, bf16 bits (x_dtype RLA_DT_BF16) or fp32: typically an Out
+ * tensor [T][Hq][128] read as H = Hq*128; w [V][H] fp32 device; tokens [T]
+ * int32 device; logp [T] fp32 device; logz [T] fp32 device or NULL.  H must be
+ * a positive multiple of 8.  A token id outside [0, V) gives logp = NaN.
+ * A token's results do not depend on the other tokens of the call.  Takes
+ * (ceil(V/64) * T * 2 + T) floats of scratch, stream-ordered, from the
+ * library's device memory pool. */
+rla_status rla_lm_head_logprobs(const void* x, rla_dtype x_dtype, const float* w, const int32_t* tokens,
+                                int32_t T, int32_t H, int32_t V, float* logp, float* logz, void* hip_stream);
+
 /* Workspace bytes rla_attn_decode_paged needs (0 on invalid arguments). */
 size_t rla_decode_workspace_bytes(const rla_attn_params* p, int32_t batch, int32_t max_context_len);
 

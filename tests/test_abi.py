@@ -186,3 +186,16 @@ def test_backward_rejects_bad_args(lib):
     # one head's query rows spanning 2 GiB (Hq=32: 2^18 rows)
     assert call(p, 1, (1 << 18) + 1, 0, (1 << 18) + 1) == 3
     assert "2 GiB" in lib.rla_last_error().decode()
+
+
+def test_lm_head_rejects_bad_args(lib):
+    """Pointers, dtype and shapes are checked before anything is enqueued."""
+    call = lambda x, dt, T, H, V, w=FAKE, lp=FAKE: lib.rla_lm_head_logprobs(x, dt, w, FAKE, T, H, V, lp, None,
+                                                                           None)
+    assert call(None, 0, 4, 64, 10) == 1
+    assert call(FAKE, 0, 4, 64, 10, w=None) == 1
+    assert call(FAKE, 0, 4, 64, 10, lp=None) == 1
+    assert call(FAKE, 7, 4, 64, 10) == 3
+    assert call(FAKE, 0, 0, 64, 10) == 2
+    assert call(FAKE, 0, 4, 12, 10) == 2      # H not a multiple of 8
+    assert call(FAKE, 0, 4, 64, 0) == 2

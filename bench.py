@@ -47,7 +47,10 @@ PROFILES = os.path.join(ROOT, "profiles")
 PREFILL_PROFILE = os.path.join(PROFILES, "prefill_kernel_b4_s4096.md")
 DECODE_PROFILE = os.path.join(PROFILES, "decode_paged_64seq.md")
 BACKWARD_PROFILE = os.path.join(PROFILES, "backward_b4_s4096.md")
+LM_HEAD_PROFILE = os.path.join(PROFILES, "lm_head_logprobs_t64_v151936.md")
 TRACE_CMD = {
+    "lm_head": "rocprofv3 --kernel-trace --stats -d gpurun_out/prof_lm_head -o run --output-format csv -- "
+               "python3 bench.py --only lm_head",
     "backward": "rocprofv3 --kernel-trace --stats -d gpurun_out/prof_backward -o run --output-format csv -- "
                 "python3 bench.py --only backward --steps 10",
     "prefill": "rocprofv3 --kernel-trace --stats -d gpurun_out/prof_prefill -o run --output-format csv -- "
@@ -57,6 +60,8 @@ TRACE_CMD = {
 }
 PMC_CMD = ("rocprofv3 --pmc {c} -d gpurun_out/pmc_{c}_{m} -o run --output-format csv -- "
            "python3 bench.py --only {m} --steps 2 --warmup 1 --decode-steps 2")
+PMC_CMD_LM_HEAD = ("rocprofv3 --pmc {c} -d gpurun_out/pmc_{c}_lm_head -o run --output-format csv -- "
+                   "python3 bench.py --only lm_head")
 PMC_CMD_BACKWARD = ("rocprofv3 --pmc {c} -d gpurun_out/pmc_{c}_backward -o run --output-format csv -- "
                     "python3 bench.py --only backward --steps 2")
 
@@ -619,6 +624,62 @@ def summarize_profiles(d):
     print(f"wrote {PREFILL_PROFILE} and {DECODE_PROFILE}")
     if os.path.isdir(os.path.join(d, "prof_backward")):
         summarize_backward(d, f_fetch, f_write, header, src)
+    if os.path.isdir(os.path.join(d, "prof_lm_head")):
+        summarize_lm_head(d, f_fetch, f_write, header, src)
+
+
+def summarize_lm_head(d, f_fetch, f_write, header, src):
+    """profiles/lm_head_logprobs_t64_v151936.md from the lm_head trace and counters."""
+    T, H, V = 64, 4096, gen.LM_VOCAB
+    flops = 2.0 * T * V * H
+    alg_bytes = V * H * 4 + T * H * 2 + T * 4 * 3
+    rows = _read_csv(os.path.join(d, "prof_lm_head", "run_kernel_stats.csv"))
+    kern = [(r["Name"], int(r["Calls"]), float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+             float(r["MaxNs"]) / 1e3) for r in rows if "lmh_" in r["Name"]]
+    kern.sort(key=lambda r: 0 if "partial" in r[0] else 1)
+    total_us = sum(r[2] for r in kern)
+
+    def counter(c, part):
+        vals = [float(r["Counter_Value"]) for r in
+                _read_csv(os.path.join(d, f"pmc_{c}_lm_head", "run_counter_collection.csv"))
+                if part in r["Kernel_Name"] and r["Counter_Name"] == c]
+        return sum(vals) / max(len(vals), 1)
+
+    lines = [
+        "# Selected log-probs through the FP32 lm_head: 64 tokens, H = 4096 (bf16 x), V = 151936",
+        "",
+        "Kernel trace (two launches per call: logits with per-block log-sum-exp partials, then the ordered fold):",
+        "",
+        "    " + TRACE_CMD["lm_head"],
+        "",
+        "| kernel | calls | avg us | min us | max us |",
+        "|---|---|---|---|---|",
+    ] + [f"| `{r[0]}` | {r[1]} | {r[2]:.1f} | {r[3]:.1f} | {r[4]:.1f} |" for r in kern] + [
+        "",
+        f"Sum of averages {total_us:.1f} us.  Algorithmic work {flops:.4e} flop (2·T·V·H FP32 MFMA) -> "
+        f"{flops / (total_us * 1e-6) / 1e12:.1f} TFLOP/s ({flops / (total_us * 1e-6) / 1e12 / PEAK_FP32_TFLOPS:.4f} of "
+        f"the 157.3 TFLOP/s dense fp32 peak); algorithmic bytes {alg_bytes} (W once, x, tokens, logp, logZ) -> "
+        f"{alg_bytes / (total_us * 1e-6) / 1e9:.1f} GB/s.",
+        "",
+        "HBM counters, one run per counter:",
+        "",
+    ] + ["    " + PMC_CMD_LM_HEAD.format(c=c) for c in ("FETCH_SIZE", "WRITE_SIZE")] + [
+        "",
+        header,
+        "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | fetch bytes | write bytes |",
+        "|---|---|---|---|---|",
+    ]
+    tot = 0
+    for part in ("lmh_partial", "lmh_fold"):
+        fk, wk = counter("FETCH_SIZE", part), counter("WRITE_SIZE", part)
+        fb, wb = int(round(fk * 1024 * f_fetch)), int(round(wk * 1024 * f_write))
+        tot += fb + wb
+        lines.append(f"| {part} | {fk:.1f} | {wk:.1f} | {fb} | {wb} |")
+    lines += ["", f"traffic bytes per call: `{tot}` ({tot / alg_bytes:.2f} x algorithmic)", "",
+              f"kernel source sha256: `{src}`", ""]
+    with open(LM_HEAD_PROFILE, "w") as f:
+        f.write("\n".join(lines))
+    print(f"wrote {LM_HEAD_PROFILE}")
 
 
 def summarize_backward(d, f_fetch, f_write, header, src):

@@ -501,15 +501,12 @@ rla_status rla_lm_head_logprobs(const void* x, rla_dtype x_dtype, const float* w
   a.T = T;
   a.H = H;
   a.V = V;
-  a.n_vblocks = (V + 63) / 64;
-  a.n_tgroups = (T + 63) / 64;
   hipStream_t s = static_cast<hipStream_t>(hip_stream);
-  const size_t bytes = (static_cast<size_t>(a.n_vblocks) * T * 2 + static_cast<size_t>(T)) * sizeof(float);
+  const size_t bytes = rla::lm_head_scratch_floats(T, V) * sizeof(float);
   void* ws = nullptr;
   hipError_t e = scratch_alloc(&ws, bytes, s);
   if (e != hipSuccess) return hip_status(e, "lm_head scratch");
-  a.part = static_cast<float*>(ws);
-  a.zsel = a.part + static_cast<size_t>(a.n_vblocks) * T * 2;
+  a.part = static_cast<float*>(ws);  // the launcher places zsel after the block partials
   e = rla::launch_lm_head(a, x_dtype == RLA_DT_FP32, s);
   const hipError_t ef = hipFreeAsync(ws, s);
   if (e != hipSuccess) return hip_status(e, "lm_head launch");

@@ -115,7 +115,7 @@ struct BackwardArgs {
 };
 
 // Selected log-probabilities through an FP32 lm_head: x [T][H] (bf16 or
-// fp32), w [V][H] fp32, tokens [T]; part [n_vblocks][T][2] and zsel [T] are
+// fp32), w [V][H] fp32, tokens [T]; part [T][n_vblocks][2] and zsel [T] are
 // scratch; logp [T], logz [T] (may be null) outputs.
 struct LmHeadArgs {
   const void* x;
@@ -126,12 +126,14 @@ struct LmHeadArgs {
   float* logp;
   float* logz;
   int32_t T, H, V;
-  int32_t n_vblocks;   // ceil(V / 64)
-  int32_t n_tgroups;   // ceil(T / 64)
+  int32_t n_vblocks;   // vocabulary blocks (set by launch_lm_head)
+  int32_t n_tgroups;   // token groups (set by launch_lm_head)
 };
 
 hipError_t launch_prefill(const PrefillArgs& a, int block, bool out_f32, bool emit, hipStream_t s);
-hipError_t launch_lm_head(const LmHeadArgs& a, bool x_f32, hipStream_t s);
+// Scratch floats launch_lm_head needs for T tokens over V rows (part + zsel).
+size_t lm_head_scratch_floats(int T, int V);
+hipError_t launch_lm_head(LmHeadArgs a, bool x_f32, hipStream_t s);
 // Pre-pass, dQ and dK/dV launches of the backward, in that order on s.
 hipError_t launch_backward(const BackwardArgs& a, bool out_f32, hipStream_t s);
 // Fused prefill with K/V gathered from paged pools (a.page_table etc. set).

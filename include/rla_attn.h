@@ -233,14 +233,14 @@ rla_status rla_attn_backward(const rla_attn_params* p, const void* q, const void
  * tokens' selected log-probs are compared; "[WS2][Attention] H100 validation
  * and reproduction guide", section "Status": decode/prefill dlogp max abs 0.0).
  * For token t: z_tv = sum_h x[t][h] * w[v][h] (FP32 MFMA accumulation in a
- * fixed order over h), logz[t] = ln sum_v exp(z_tv) (per-64-row block max and
+ * fixed order over h), logz[t] = ln sum_v exp(z_tv) (per-32-row block max and
  * sum, folded in ascending block order), logp[t] = z_{t,tokens[t]} - logz[t].
  * x [T][H] device, bf16 bits (x_dtype RLA_DT_BF16) or fp32: typically an Out
  * tensor [T][Hq][128] read as H = Hq*128; w [V][H] fp32 device; tokens [T]
  * int32 device; logp [T] fp32 device; logz [T] fp32 device or NULL.  H must be
  * a positive multiple of 8.  A token id outside [0, V) gives logp = NaN.
  * A token's results do not depend on the other tokens of the call.  Takes
- * (ceil(V/64) * T * 2 + T) floats of scratch, stream-ordered, from the
+ * (ceil(V/32) * T * 2 + T) floats of scratch, stream-ordered, from the
  * library's device memory pool. */
 rla_status rla_lm_head_logprobs(const void* x, rla_dtype x_dtype, const float* w, const int32_t* tokens,
                                 int32_t T, int32_t H, int32_t V, float* logp, float* logz, void* hip_stream);

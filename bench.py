@@ -189,7 +189,7 @@ def reported_legs(api, up, stream):
     return res
 
 
-def backward_leg(api, cfg, qd, kd, vd, up, stream, steps):
+def backward_leg(api, cfg, qd, kd, vd, up, stream, steps, cpu_q=None):
     """Backward (dQ, dK, dV) of the same causal prefill: pre-pass, dQ and dK/dV
     launches timed together with events on the launch stream.  Algorithmic
     flops: the five products QK^T, dOut V^T, P^T dOut, dS^T Q, dS K over the
@@ -218,15 +218,35 @@ def backward_leg(api, cfg, qd, kd, vd, up, stream, steps):
     flops = 2.5 * cfg.flops()
     del do, out, lse, dq, dk, dv
     torch.cuda.empty_cache()
-    return {"tflops": round(flops / (ms * 1e-3) / 1e12, 2), "ms": round(ms, 4),
-            "frac_of_peak": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4), "flop_per_step": flops,
-            "workload": "backward of causal prefill B=4 S=4096 Hq=32 Hkv=8 D=128, bf16 in, fp32 dQ/dK/dV"}
+    res = {"tflops": round(flops / (ms * 1e-3) / 1e12, 2), "ms": round(ms, 4),
+           "frac_of_peak": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4), "flop_per_step": flops,
+           "workload": "backward of causal prefill B=4 S=4096 Hq=32 Hkv=8 D=128, bf16 in, fp32 dQ/dK/dV"}
+    if cpu_q is not None:
+        res["cpu_baseline"] = backward_cpu_baseline(cfg, *cpu_q)
+    return res
+
+
+def backward_cpu_baseline(cfg, q, k, v, do, n_rows=48):
+    """The FP64 oracle's backward on a seeded sample of query rows of the same
+    workload (their complete dQ and their dK/dV terms), in algorithmic flops:
+    10*D per visible (row, key) pair and q head."""
+    import oracle
+    rng = np.random.Generator(np.random.PCG64(77))
+    rows = np.unique(rng.integers(0, cfg.B * cfg.S, n_rows))
+    t = rows % cfg.S
+    flops = float(np.sum(10.0 * cfg.D * cfg.Hq * (t + 1)))
+    t0 = time.perf_counter()
+    oracle.attention_backward(q, k, v, do, scale=cfg.softmax_scale, rows=rows)
+    dt = time.perf_counter() - t0
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.oracle_threads(),
+            "kind": "oracle", "sample": f"{rows.size} seeded query rows x all {cfg.Hq} heads of the B=4 S=4096 "
+                                        f"backward ({flops:.3e} flop, {dt:.1f} s, FP64)"}
 
 
 PEAK_FP32_TFLOPS = 157.3   # MI355X dense fp32 MFMA (published)
 
 
-def lm_head_leg(api, up, stream, reps=5):
+def lm_head_leg(api, up, stream, reps=5, cpu=False):
     """Selected log-probs of 64 active tokens (one per decode sequence, the
     attention output of all 32 heads: H = 4096) through a synthetic FP32
     lm_head over Qwen3-8B's 151936-token vocabulary: one pass over W (2.49 GB)
@@ -234,7 +254,8 @@ def lm_head_leg(api, up, stream, reps=5):
     import torch
     T, H, V = 64, 4096, gen.LM_VOCAB
     log("generating the synthetic lm_head (151936 x 4096 fp32)")
-    w = torch.from_numpy(gen.lm_head_weights(V, H)).to(stream.device)
+    w_host = gen.lm_head_weights(V, H)
+    w = torch.from_numpy(w_host).to(stream.device)
     x = up(gen.draw_bf16(1000 * 4 + 11, (T, H)))
     tok = torch.from_numpy(gen.lm_tokens(T, V)).to(stream.device)
     api.lm_head_logprobs(x, w, tok)
@@ -249,12 +270,25 @@ def lm_head_leg(api, up, stream, reps=5):
     ms = e0.elapsed_time(e1) / reps
     flops = 2.0 * T * V * H
     wbytes = V * H * 4
-    del w, x, tok
+    del w, tok
     torch.cuda.empty_cache()
-    return {"ms": round(ms, 4), "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
-            "frac_of_fp32_peak": round(flops / (ms * 1e-3) / 1e12 / PEAK_FP32_TFLOPS, 4),
-            "w_gbs": round(wbytes / (ms * 1e-3) / 1e9, 1),
-            "workload": "selected log-probs, 64 tokens x H=4096 bf16 through an fp32 lm_head of 151936 rows"}
+    res = {"ms": round(ms, 4), "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+           "frac_of_fp32_peak": round(flops / (ms * 1e-3) / 1e12 / PEAK_FP32_TFLOPS, 4),
+           "w_gbs": round(wbytes / (ms * 1e-3) / 1e9, 1),
+           "workload": "selected log-probs, 64 tokens x H=4096 bf16 through an fp32 lm_head of 151936 rows"}
+    if cpu:
+        import oracle
+        n = 8  # a bounded sample: the first 8 of the 64 tokens
+        xs = x[:n].view(torch.int16).cpu().numpy().view(np.uint16)
+        t0 = time.perf_counter()
+        oracle.lm_head_logprobs(xs, w_host, gen.lm_tokens(T, V)[:n])
+        dt = time.perf_counter() - t0
+        f = 2.0 * n * V * H
+        res["cpu_baseline"] = {"value": round(f / dt / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.oracle_threads(),
+                               "kind": "oracle", "sample": f"{n} of the 64 tokens over the full vocabulary "
+                                                           f"({f:.3e} flop, {dt:.1f} s, FP64)"}
+    del x
+    return res
 
 
 def main():
@@ -365,7 +399,8 @@ def main():
     backward = None
     if args.only is None:
         log("backward")
-        backward = backward_leg(api, cfg, qd, kd, vd, up, stream, 10)
+        backward = backward_leg(api, cfg, qd, kd, vd, up, stream, 10,
+                                cpu_q=None if args.no_cpu_baseline else (q, k, v, gen.dout_inputs(cfg)))
         log(f"backward {backward['ms']:.3f} ms, {backward['tflops']:.1f} TFLOP/s")
     del qd, kd, vd, out
     torch.cuda.empty_cache()
@@ -376,7 +411,7 @@ def main():
     reported = None if args.no_reported else reported_legs(api, up, stream)
     lm_head = None
     if not args.no_reported:
-        lm_head = lm_head_leg(api, up, stream)
+        lm_head = lm_head_leg(api, up, stream, cpu=not args.no_cpu_baseline)
         log(f"lm_head {lm_head['ms']:.3f} ms, {lm_head['tflops']:.1f} TFLOP/s fp32")
 
     line = {

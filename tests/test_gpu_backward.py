@@ -195,3 +195,44 @@ def test_backward_full_size_sampled():
     assert_bitwise(torch.cat(dqs, dim=1), dq, "full-size replay dQ")
     assert_bitwise(dk2, dk, "full-size replay dK")
     assert_bitwise(dv2, dv, "full-size replay dV")
+
+
+@pytest.mark.slow
+def test_backward_long_context_zigzag_replay():
+    """The long-context workload (B=1, S=32768, Q and K drawn x4, causal):
+    dQ of sampled rows against the oracle, the dV row-sum identity, and a
+    replay of the query rows in the zigzag CP=2 ownership order (shard 0 owns
+    quarters 0 and 3, shard 1 quarters 1 and 2; dK/dV handed on in ascending
+    row order) bitwise equal to one call."""
+    cfg = gen.CFG5
+    q, k, v = gen.prefill_inputs(cfg)
+    do = gen.dout_inputs(cfg)
+    scale = cfg.softmax_scale
+    S = cfg.S
+    say(f"[backward] long context S={S}")
+    qd, kd, vd, dod = dev_bf16(q), dev_bf16(k), dev_bf16(v), dev_bf16(do)
+    out, lse = api.prefill(qd, kd, vd, block=cfg.block, scale=scale)
+    dq, dk, dv = api.backward(qd, kd, vd, out, lse, dod, scale=scale)
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 127, 128, 8191, 8192, 16383, 16384, 24575, 24576, 32766, 32767], np.int64)
+    rq, _, _, mq, _, _ = oracle.attention_backward(q, k, v, do, scale=scale, rows=rows, mags=True)
+    _check(dq.reshape(S, cfg.Hq, 128)[rows], rq.reshape(S, cfg.Hq, 128)[rows],
+           mq.reshape(S, cfg.Hq, 128)[rows], "long-context dQ rows")
+    g = cfg.Hq // cfg.Hkv
+    dof = gen.bf16_bits_to_f32(do).astype(np.float64).reshape(1, S, cfg.Hkv, g, 128)
+    got = host_f64(dv).sum(axis=1)
+    assert (np.abs(got - dof.sum(axis=(1, 3))) <= 2.0 ** -7 * np.abs(dof).sum(axis=(1, 3)) + 1e-6).all()
+    quarter = S // 4
+    dk2 = torch.zeros_like(dk)
+    dv2 = torch.zeros_like(dv)
+    dq2 = torch.empty_like(dq)
+    for owner, c in ((0, 0), (1, 1), (1, 2), (0, 3)):  # ascending rows, alternating owners
+        c0, c1 = c * quarter, (c + 1) * quarter
+        say(f"    shard {owner} rows [{c0}, {c1})")
+        part, _, _ = api.backward(qd[:, c0:c1].contiguous(), kd, vd, out[:, c0:c1].contiguous(),
+                                  lse[:, c0:c1].contiguous(), dod[:, c0:c1].contiguous(), cache_len=c0, scale=scale,
+                                  dk=dk2, dv=dv2, accumulate=True)
+        dq2[:, c0:c1] = part
+    assert_bitwise(dq2, dq, "zigzag replay dQ")
+    assert_bitwise(dk2, dk, "zigzag replay dK")
+    assert_bitwise(dv2, dv, "zigzag replay dV")

@@ -18,10 +18,10 @@
 // two halves of the wave cover a 128-byte line), three visits ahead of the
 // MFMAs.  Pass 1 writes, per (32-row vocabulary block, token), the block max
 // and the fixed-tree sum of exp(z - max) (and the selected logit from the
-// block that holds y_t); pass 2 folds the blocks in ascending order:
-// M = max of the block maxima, S = sum_b s_b exp(m_b - M) with lane l taking
-// blocks l, l+64, ... in order and a fixed butterfly across lanes,
-// logZ = M + ln S.
+// block that holds y_t); pass 2 folds the blocks: M = max of the block
+// maxima, S = sum_b s_b exp(m_b - M) in a fixed order (four contiguous
+// quarters, lanes strided in ascending order inside each, fixed trees
+// across lanes and quarters), logZ = M + ln S.
 #include <type_traits>
 
 #include "kernels.hpp"
@@ -192,18 +192,27 @@ __global__ __launch_bounds__(kWaves * 64) void lmh_partial_kernel(const LmHeadAr
   }
 }
 
-// Pass 2: one wave per token.
+// Pass 2: one workgroup of 4 waves per token.  Wave w takes the blocks
+// [w*n/4, (w+1)*n/4), lane l of it blocks l, l+64, ... of that range in
+// ascending order; the lanes' sums meet in a fixed butterfly and the four
+// wave sums as (s0 + s1) + (s2 + s3).
 __global__ __launch_bounds__(256) void lmh_fold_kernel(const LmHeadArgs a) {
+  __shared__ float red[8];
   const int lane = threadIdx.x & 63;
-  const int t = static_cast<int>(blockIdx.x) * 4 + static_cast<int>(threadIdx.x >> 6);
-  if (t >= a.T) return;
-  float mx = kNegInf;
+  const int wave = threadIdx.x >> 6;
+  const int t = static_cast<int>(blockIdx.x);
   const float* part = a.part + static_cast<int64_t>(t) * a.n_vblocks * 2;
-  for (int b = lane; b < a.n_vblocks; b += 64) mx = fmaxf(mx, part[2 * b]);
+  const int lo = static_cast<int>(static_cast<int64_t>(a.n_vblocks) * wave / 4);
+  const int hi = static_cast<int>(static_cast<int64_t>(a.n_vblocks) * (wave + 1) / 4);
+  float mx = kNegInf;
+  for (int b = lo + lane; b < hi; b += 64) mx = fmaxf(mx, part[2 * b]);
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) mx = fmaxf(mx, __shfl_xor(mx, m, 64));
+  if (lane == 0) red[wave] = mx;
+  __syncthreads();
+  mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   float s = 0.0f;
-  for (int b = lane; b < a.n_vblocks; b += 64) {
+  for (int b = lo + lane; b < hi; b += 64) {
     const float2 p = *reinterpret_cast<const float2*>(part + 2 * b);
     const float w = hw_exp2((p.x - mx) * kLog2e);
     const float term = p.y * w;
@@ -212,8 +221,11 @@ __global__ __launch_bounds__(256) void lmh_fold_kernel(const LmHeadArgs a) {
   // Butterfly: lanes i and i^m add the same two values, so all lanes agree.
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) s = s + __shfl_xor(s, m, 64);
-  if (lane == 0) {
-    const float lz = mx + hw_log2(s) * kLn2;
+  if (lane == 0) red[4 + wave] = s;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const float tot = (red[4] + red[5]) + (red[6] + red[7]);
+    const float lz = mx + hw_log2(tot) * kLn2;
     const int y = a.tokens[t];
     const float lp = (y >= 0 && y < a.V) ? a.zsel[t] - lz : __builtin_nanf("");
     a.logp[t] = lp;
@@ -242,8 +254,7 @@ hipError_t launch_lm_head(LmHeadArgs a, bool x_f32, hipStream_t s) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t g2 = (static_cast<int64_t>(a.T) + 3) / 4;
-  hipLaunchKernelGGL(lmh_fold_kernel, dim3(static_cast<unsigned>(g2)), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(lmh_fold_kernel, dim3(static_cast<unsigned>(a.T)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

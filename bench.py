@@ -190,7 +190,7 @@ def reported_legs(api, up, stream):
 
 
 def backward_leg(api, cfg, qd, kd, vd, up, stream, steps, cpu_q=None):
-    """Backward (dQ, dK, dV) of the same causal prefill: pre-pass, dQ and dK/dV
+    """Backward (dQ, dK, dV) of the same causal prefill: the dQ and dK/dV
     launches timed together with events on the launch stream.  Algorithmic
     flops: the five products QK^T, dOut V^T, P^T dOut, dS^T Q, dS K over the
     unmasked pairs, 2.5x the forward's."""
@@ -723,11 +723,11 @@ def summarize_backward(d, f_fetch, f_write, header, src):
     rows = _read_csv(os.path.join(d, "prof_backward", "run_kernel_stats.csv"))
     kern = [(r["Name"], int(r["Calls"]), float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
              float(r["MaxNs"]) / 1e3) for r in rows if "bwd_" in r["Name"]]
-    order = {"bwd_prep": 0, "bwd_dq": 1, "bwd_dkdv": 2}
+    order = {"bwd_dq": 0, "bwd_dkdv": 1}
     kern.sort(key=lambda r: min(v for k, v in order.items() if k in r[0]))
     fwd = cfg.flops()
     alg = 2.5 * fwd
-    executed = {"bwd_prep": 0.0, "bwd_dq": 1.5 * fwd, "bwd_dkdv": 2.0 * fwd}
+    executed = {"bwd_dq": 1.5 * fwd, "bwd_dkdv": 2.0 * fwd}
     B, S, Hq, Hkv, D = cfg.B, cfg.S, cfg.Hq, cfg.Hkv, cfg.D
     alg_bytes = B * S * (3 * Hq + 2 * Hkv) * D * 2 + B * S * Hq * 4 + B * S * (Hq + 2 * Hkv) * D * 4
     total_us = sum(r[2] for r in kern)
@@ -742,7 +742,7 @@ def summarize_backward(d, f_fetch, f_write, header, src):
     lines = [
         "# Backward (dQ, dK, dV), causal B=4 S=4096 Hq=32 Hkv=8 D=128, bf16 in, fp32 gradients",
         "",
-        "Kernel trace (three launches per backward call: pre-pass, dQ, dK/dV):",
+        "Kernel trace (two launches per backward call: dQ, which also writes Delta per row, then dK/dV):",
         "",
         "    " + TRACE_CMD["backward"],
         "",
@@ -772,7 +772,7 @@ def summarize_backward(d, f_fetch, f_write, header, src):
         "|---|---|---|---|---|",
     ]
     tot = 0
-    for part in ("bwd_prep", "bwd_dq", "bwd_dkdv"):
+    for part in ("bwd_dq", "bwd_dkdv"):
         fk, _ = counter("FETCH_SIZE", part)
         wk, _ = counter("WRITE_SIZE", part)
         fb, wb = int(round(fk * 1024 * f_fetch)), int(round(wk * 1024 * f_write))

@@ -20,9 +20,9 @@
 //    ascending order.  One workgroup owns 128 keys for the whole walk.
 //  * dQ of a row: KV blocks of 64 keys in ascending order from key 0, each in
 //    four 16-key MFMA steps.
-// Three launches: a pre-pass writes LSE * log2 e and Delta per row (Delta is
-// a fixed lane-butterfly sum of the 128 products), then the dQ kernel and
-// the dK/dV kernel.  Chunked replay: with accumulate set, dK/dV start from the
+// Two launches: the dQ kernel, which also computes Delta per row (a fixed
+// tree over the 128 products) and writes it with LSE * log2 e to a per-row
+// scratch, then the dK/dV kernel.  Chunked replay: with accumulate set, dK/dV start from the
 // values already in the output buffers, so calls over consecutive query
 // chunks whose boundaries are multiples of 64 rows continue the chains of a
 // single call over all rows and give its exact bits.
@@ -73,59 +73,6 @@ __device__ __forceinline__ bf16x8 pack8(const f32x16& x, int s) {
   return as_bf16x8(w);
 }
 
-// ------------------------------------------------------------- pre-pass --
-
-// 16 lanes per (b, h, t) row, t < Sq_pad (four rows per wave): lane l of the
-// row takes dims 8l..8l+7; the eight products are summed in a fixed tree,
-// then the 16 lanes' sums by a butterfly.
-template <bool OUT_F32>
-__global__ __launch_bounds__(256) void bwd_prep_kernel(const BackwardArgs a) {
-  const int sub = threadIdx.x & 15;
-  const int64_t item = static_cast<int64_t>(blockIdx.x) * 16 + (threadIdx.x >> 4);
-  const int64_t total = static_cast<int64_t>(a.B) * a.Hq * a.Sq_pad;
-  const bool live = item < total;
-  const int64_t it = live ? item : 0;
-  const int t = static_cast<int>(it % a.Sq_pad);
-  const int64_t bh = it / a.Sq_pad;
-  const int h = static_cast<int>(bh % a.Hq);
-  const int b = static_cast<int>(bh / a.Hq);
-  float x = 0.0f;
-  float lse2 = 0.0f;
-  if (live && t < a.Sq) {
-    const int64_t e = static_cast<int64_t>(b) * a.q_bstride + (static_cast<int64_t>(t) * a.Hq + h) * kHeadDim + 8 * sub;
-    const u32x4 gw = *reinterpret_cast<const u32x4*>(a.dout + e);
-    float o[8];
-    if constexpr (OUT_F32) {
-      const f32x4 o0 = *reinterpret_cast<const f32x4*>(static_cast<const float*>(a.out) + e);
-      const f32x4 o1 = *reinterpret_cast<const f32x4*>(static_cast<const float*>(a.out) + e + 4);
-      for (int i = 0; i < 4; ++i) {
-        o[i] = o0[i];
-        o[4 + i] = o1[i];
-      }
-    } else {
-      const u32x4 ow = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.out) + e);
-      for (int i = 0; i < 4; ++i) {
-        o[2 * i] = bf16_lo_to_f32(ow[i]);
-        o[2 * i + 1] = bf16_hi_to_f32(ow[i]);
-      }
-    }
-    float p[8];
-    for (int i = 0; i < 4; ++i) {
-      p[2 * i] = bf16_lo_to_f32(gw[i]) * o[2 * i];
-      p[2 * i + 1] = bf16_hi_to_f32(gw[i]) * o[2 * i + 1];
-    }
-    x = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-    lse2 = a.lse[(static_cast<int64_t>(b) * a.Sq + t) * a.Hq + h] * kLog2e;
-  }
-#pragma unroll
-  for (int m = 8; m >= 1; m >>= 1) x = x + __shfl_xor(x, m, 64);
-  if (live && sub == 0) {
-    float* row = a.ws + bh * 2 * a.Sq_pad;
-    row[t] = lse2;
-    row[a.Sq_pad + t] = x;
-  }
-}
-
 // ----------------------------------------------------------------- dQ --
 
 // One workgroup of 8 waves per (b, kv head, head subgroup, query tile of 64
@@ -135,6 +82,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const BackwardArgs a) {
 // reads for dP^T), double-buffered.
 constexpr int kDqWaves = 8;
 
+template <bool OUT_F32>
 __global__ __launch_bounds__(kDqWaves * 64) void bwd_dq_kernel(const BackwardArgs a) {
   using Ld = BlockLoader<kQB, kDqWaves>;
   constexpr int kRegion = kQB * kHeadDim * 2;
@@ -174,11 +122,54 @@ __global__ __launch_bounds__(kDqWaves * 64) void bwd_dq_kernel(const BackwardArg
       of[ds] = as_bf16x8(q_ok ? gload16(a.dout + e + 16 * ds) : u32x4{0, 0, 0, 0});
     }
   }
+  // Delta of the lane's row: the products dOut * Out of the dims the lane
+  // holds (16ds + 8half + 0..7) in a fixed tree per D-step, the eight step
+  // sums in a fixed tree, then the partner lane's sum (the other half of the
+  // row).  LSE * log2 e and Delta go to the scratch for the dK/dV kernel
+  // (zeros for rows past Sq).
   float lse2 = 0.0f, delta = 0.0f;
-  if (q_ok) {
-    const float* row = a.ws + (static_cast<int64_t>(b) * a.Hq + head) * 2 * a.Sq_pad;
-    lse2 = row[t];
-    delta = row[a.Sq_pad + t];
+  {
+    float part = 0.0f;
+    if (q_ok) {
+      const int64_t e = static_cast<int64_t>(b) * a.q_bstride + (static_cast<int64_t>(t) * a.Hq + head) * kHeadDim + 8 * half;
+      float st[kDSteps];
+#pragma unroll
+      for (int ds = 0; ds < kDSteps; ++ds) {
+        float o[8];
+        if constexpr (OUT_F32) {
+          const f32x4 o0 = *reinterpret_cast<const f32x4*>(static_cast<const float*>(a.out) + e + 16 * ds);
+          const f32x4 o1 = *reinterpret_cast<const f32x4*>(static_cast<const float*>(a.out) + e + 16 * ds + 4);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            o[i] = o0[i];
+            o[4 + i] = o1[i];
+          }
+        } else {
+          const u32x4 ow = gload16(static_cast<const uint16_t*>(a.out) + e + 16 * ds);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            o[2 * i] = bf16_lo_to_f32(ow[i]);
+            o[2 * i + 1] = bf16_hi_to_f32(ow[i]);
+          }
+        }
+        const u32x4 gw = __builtin_bit_cast(u32x4, of[ds]);
+        float p[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          p[2 * i] = bf16_lo_to_f32(gw[i]) * o[2 * i];
+          p[2 * i + 1] = bf16_hi_to_f32(gw[i]) * o[2 * i + 1];
+        }
+        st[ds] = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+      }
+      part = ((st[0] + st[1]) + (st[2] + st[3])) + ((st[4] + st[5]) + (st[6] + st[7]));
+      lse2 = a.lse[(static_cast<int64_t>(b) * a.Sq + t) * a.Hq + head] * kLog2e;
+    }
+    delta = pair_sum(part);
+    if (wave_used && half == 0) {
+      float* row = a.ws + (static_cast<int64_t>(b) * a.Hq + head) * 2 * a.Sq_pad;
+      row[t] = lse2;
+      row[a.Sq_pad + t] = delta;
+    }
   }
 
   const int64_t n_kv_blocks = (a.kv_len + kQB - 1) / kQB;
@@ -519,24 +510,16 @@ void bwd_dkdv_kernel(const BackwardArgs a) {
 }  // namespace
 
 hipError_t launch_backward(const BackwardArgs& a, bool out_f32, hipStream_t s) {
-  // pre-pass
-  const int64_t rows = static_cast<int64_t>(a.B) * a.Hq * a.Sq_pad;
-  const int64_t g0 = (rows + 15) / 16;
-  if (g0 <= 0 || g0 > 0x7fffffff) return hipErrorInvalidConfiguration;
+  // dQ (also writes LSE * log2 e and Delta per row), then dK / dV
+  const int64_t g1 = static_cast<int64_t>(a.B) * a.Hkv * a.hsubs * a.n_qtiles;
+  if (g1 <= 0 || g1 > 0x7fffffff) return hipErrorInvalidConfiguration;
   if (out_f32) {
-    hipLaunchKernelGGL((bwd_prep_kernel<true>), dim3(static_cast<unsigned>(g0)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(bwd_dq_kernel<true>, dim3(static_cast<unsigned>(g1)), dim3(kDqWaves * 64), 0, s, a);
   } else {
-    hipLaunchKernelGGL((bwd_prep_kernel<false>), dim3(static_cast<unsigned>(g0)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(bwd_dq_kernel<false>, dim3(static_cast<unsigned>(g1)), dim3(kDqWaves * 64), 0, s, a);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // dQ
-  const int64_t g1 = static_cast<int64_t>(a.B) * a.Hkv * a.hsubs * a.n_qtiles;
-  if (g1 > 0x7fffffff) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(bwd_dq_kernel, dim3(static_cast<unsigned>(g1)), dim3(kDqWaves * 64), 0, s, a);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  // dK / dV
   const int64_t g2 = static_cast<int64_t>(a.B) * a.Hkv * a.n_kblocks;
   if (g2 <= 0) return hipSuccess;
   if (g2 > 0x7fffffff) return hipErrorInvalidConfiguration;

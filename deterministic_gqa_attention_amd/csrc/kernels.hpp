@@ -134,7 +134,7 @@ hipError_t launch_prefill(const PrefillArgs& a, int block, bool out_f32, bool em
 // Scratch floats launch_lm_head needs for T tokens over V rows (part + zsel).
 size_t lm_head_scratch_floats(int T, int V);
 hipError_t launch_lm_head(LmHeadArgs a, bool x_f32, hipStream_t s);
-// Pre-pass, dQ and dK/dV launches of the backward, in that order on s.
+// The dQ and dK/dV launches of the backward, in that order on s.
 hipError_t launch_backward(const BackwardArgs& a, bool out_f32, hipStream_t s);
 // Fused prefill with K/V gathered from paged pools (a.page_table etc. set).
 hipError_t launch_prefill_paged(const PrefillArgs& a, int block, bool out_f32, hipStream_t s);

@@ -101,6 +101,38 @@ def test_backward_parity_chunk_after_cache():
     _parity_case(41, 2, 72, 8, 2, cache_len=128, s_max=256, what="chunk after cache")
 
 
+def test_backward_parity_noncausal_chunk():
+    """A non-causal chunk of 72 queries after 64 cached keys (every query sees
+    all 136 keys) in a cache of 200 slots."""
+    _parity_case(43, 2, 72, 8, 2, cache_len=64, s_max=200, causal=False, what="non-causal chunk")
+
+
+def test_backward_noncausal_replay_bitwise():
+    """Non-causal replay: rows [0,128) then [128,200), each chunk seeing all
+    200 keys, accumulate into dK/dV and give the single call's bits."""
+    B, S, Hq, Hkv = 1, 200, 8, 2
+    q, k, v, do = _inputs(44, B, S, S, Hq, Hkv)
+    scale = 1.0 / np.sqrt(128.0)
+    qd, kd, vd, dod = dev_bf16(q), dev_bf16(k), dev_bf16(v), dev_bf16(do)
+    out, lse = api.prefill(qd, kd, vd, block=128, causal=False, scale=scale)
+    ref = api.backward(qd, kd, vd, out, lse, dod, causal=False, scale=scale)
+    dk = torch.zeros_like(ref[1])
+    dv = torch.zeros_like(ref[2])
+    dqs = []
+    for c0, c1 in ((0, 128), (128, 200)):
+        # a chunk sees the keys [0, cache_len + rows): with cache_len = S - rows
+        # that is all S keys, as in the single call (without a causal mask the
+        # rows' positions do not matter)
+        n = c1 - c0
+        dq_c, _, _ = api.backward(qd[:, c0:c1].contiguous(), kd, vd, out[:, c0:c1].contiguous(),
+                                  lse[:, c0:c1].contiguous(), dod[:, c0:c1].contiguous(), cache_len=S - n,
+                                  causal=False, scale=scale, dk=dk, dv=dv, accumulate=True)
+        dqs.append(dq_c)
+    assert_bitwise(torch.cat(dqs, dim=1), ref[0], "non-causal replay dQ")
+    assert_bitwise(dk, ref[1], "non-causal replay dK")
+    assert_bitwise(dv, ref[2], "non-causal replay dV")
+
+
 def test_backward_parity_peaky_scores():
     """Large scores (Q and K scaled by 4): probabilities near 0 and 1, where dS
     is most sensitive to the rounding of P."""

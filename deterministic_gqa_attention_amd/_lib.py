@@ -73,7 +73,7 @@ def load(path: str = LIB_PATH):
     lib.rla_attn_decode_paged.argtypes = [pp, P, P, P, i64, i32, P, i32, P, ctypes.POINTER(ctypes.c_int32),
                                           i32, i32, P, sz, P, P, P]
     lib.rla_attn_decode_paged.restype = ctypes.c_int
-    lib.rla_attn_backward.argtypes = [pp, P, P, P, P, P, P, i32, i32, i32, i32, i32, P, P, P, P]
+    lib.rla_attn_backward.argtypes = [pp, P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, P, P, P, P]
     lib.rla_attn_backward.restype = ctypes.c_int
     lib.rla_lm_head_logprobs.argtypes = [P, i32, P, P, i32, i32, i32, P, P, P]
     lib.rla_lm_head_logprobs.restype = ctypes.c_int

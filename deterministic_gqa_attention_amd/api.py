@@ -123,31 +123,34 @@ def prefill_paged(q_chunk, k_pool, v_pool, page_table, *, cache_len, block, out_
 
 
 def backward(q, k, v, out, lse, dout, *, cache_len=0, causal=True, scale=None, dq=None, dk=None, dv=None,
-             accumulate=False):
+             accumulate=False, grad_dtype=torch.float32):
     """dQ, dK, dV of Out for (chunked) prefill.
 
     q, dout [B,C,Hq,128] bf16; k, v [B,S_max,Hkv,128] bf16 (keys [0, cache_len+C)
     used); out [B,C,Hq,128] (bf16 or fp32, the forward output); lse [B,C,Hq] fp32.
-    Returns (dq [B,C,Hq,128], dk, dv [B,S_max,Hkv,128]) in fp32; dk/dv rows past
-    cache_len+C are left as given (zeros when allocated here).  With
-    ``accumulate`` the call adds to the given dk/dv."""
+    Returns (dq [B,C,Hq,128], dk, dv [B,S_max,Hkv,128]) in grad_dtype (fp32, or
+    bf16 rounded once from the fp32 result); dk/dv rows past cache_len+C are left
+    as given (zeros when allocated here).  With ``accumulate`` (fp32 only) the
+    call adds to the given dk/dv."""
     B, C, Hq, D = q.shape
     S_max, Hkv = k.shape[1], k.shape[2]
     if out.dtype not in _OUT_DT:
         raise ValueError(f"out must be bf16 or fp32, got {out.dtype}")
     p = params(Hq, Hkv, block=128, out_dtype=out.dtype, causal=causal, scale=scale, head_dim=D)
-    dq = torch.empty((B, C, Hq, D), dtype=torch.float32, device=q.device) if dq is None else dq
+    if grad_dtype not in _OUT_DT:
+        raise ValueError(f"grad_dtype must be bfloat16 or float32, got {grad_dtype}")
+    dq = torch.empty((B, C, Hq, D), dtype=grad_dtype, device=q.device) if dq is None else dq
     if dk is None:
-        dk = torch.zeros((B, S_max, Hkv, D), dtype=torch.float32, device=q.device)
+        dk = torch.zeros((B, S_max, Hkv, D), dtype=grad_dtype, device=q.device)
     if dv is None:
-        dv = torch.zeros((B, S_max, Hkv, D), dtype=torch.float32, device=q.device)
+        dv = torch.zeros((B, S_max, Hkv, D), dtype=grad_dtype, device=q.device)
     lib = _lib.load()
     _lib.check(lib.rla_attn_backward(
         ctypes.byref(p), _dev(q, "q", torch.bfloat16, 4), _dev(k, "k", torch.bfloat16, 4),
         _dev(v, "v", torch.bfloat16, 4), _dev(out, "out", out.dtype, 4), _dev(lse, "lse", torch.float32, 3),
         _dev(dout, "dout", torch.bfloat16, 4), B, C, int(cache_len), S_max, int(bool(accumulate)),
-        _dev(dq, "dq", torch.float32, 4), _dev(dk, "dk", torch.float32, 4), _dev(dv, "dv", torch.float32, 4),
-        _stream(q.device)))
+        _OUT_DT[grad_dtype], _dev(dq, "dq", grad_dtype, 4), _dev(dk, "dk", grad_dtype, 4),
+        _dev(dv, "dv", grad_dtype, 4), _stream(q.device)))
     return dq, dk, dv
 
 

@@ -422,7 +422,7 @@ rla_status rla_attn_decode_paged(const rla_attn_params* p, const void* q, const 
 rla_status rla_attn_backward(const rla_attn_params* p, const void* q, const void* k, const void* v,
                              const void* out, const float* lse, const void* dout, int32_t batch,
                              int32_t q_rows, int32_t cache_len, int32_t s_max, int32_t accumulate,
-                             float* dq, float* dk, float* dv, void* hip_stream) {
+                             rla_dtype grad_dtype, void* dq, void* dk, void* dv, void* hip_stream) {
   int g = 0;
   rla_status st = check_params(p, true, &g);
   if (st != RLA_OK) return st;
@@ -433,6 +433,10 @@ rla_status rla_attn_backward(const rla_attn_params* p, const void* q, const void
     return fail(RLA_ERR_BAD_SHAPE, "need batch>=1, q_rows>=1, cache_len>=0, cache_len+q_rows<=s_max "
                 "(got %d, %d, %d, %d)", batch, q_rows, cache_len, s_max);
   if (accumulate != 0 && accumulate != 1) return fail(RLA_ERR_BAD_SHAPE, "accumulate must be 0 or 1");
+  if (grad_dtype != RLA_DT_BF16 && grad_dtype != RLA_DT_FP32)
+    return fail(RLA_ERR_UNSUPPORTED, "grad_dtype=%d unsupported", grad_dtype);
+  if (accumulate && grad_dtype != RLA_DT_FP32)
+    return fail(RLA_ERR_UNSUPPORTED, "accumulate needs fp32 gradients (the running sums are fp32)");
   const int Hq = p->num_q_heads, Hkv = p->num_kv_heads, D = rla::kHeadDimPublic;
   const int64_t kv_len = static_cast<int64_t>(cache_len) + q_rows;
   // Sq_pad = q_rows rounded up to the 64-row tile; its rows must fit the
@@ -469,6 +473,7 @@ rla_status rla_attn_backward(const rla_attn_params* p, const void* q, const void
   a.n_kblocks = static_cast<int32_t>((kv_len + 127) / 128);
   a.causal = p->causal;
   a.accumulate = accumulate;
+  a.grad_bf16 = grad_dtype == RLA_DT_BF16;
   a.c = score_scale(p);
   a.scale = p->softmax_scale;
 

@@ -62,6 +62,16 @@ struct RowReadsV {
   }
 };
 
+// Four consecutive gradient values at element idx of an fp32 or bf16 (RNE,
+// the only rounding of the result) output.
+__device__ __forceinline__ void store_grad4(void* base, int64_t idx, float x0, float x1, float x2, float x3, bool bf) {
+  if (bf) {
+    *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(base) + idx) = u32x2{pack_bf16(x0, x1), pack_bf16(x2, x3)};
+  } else {
+    *reinterpret_cast<f32x4*>(static_cast<float*>(base) + idx) = f32x4{x0, x1, x2, x3};
+  }
+}
+
 // Eight accumulator registers 8s..8s+7 rounded to bf16 as one MFMA
 // B-fragment (element j = register 8s + j).
 __device__ __forceinline__ bf16x8 pack8(const f32x16& x, int s) {
@@ -274,14 +284,14 @@ __global__ __launch_bounds__(kDqWaves * 64) void bwd_dq_kernel(const BackwardArg
 
   if (!q_ok) return;
   // acc[dt] register v: dim 32dt + 8(v/4) + 4half + v%4 of row t.
-  float* dst = a.dq + static_cast<int64_t>(b) * a.q_bstride + (static_cast<int64_t>(t) * a.Hq + head) * kHeadDim + 4 * half;
+  const int64_t dst = static_cast<int64_t>(b) * a.q_bstride + (static_cast<int64_t>(t) * a.Hq + head) * kHeadDim + 4 * half;
+  const bool gbf = a.grad_bf16 != 0;
 #pragma unroll
   for (int dt = 0; dt < kDTiles; ++dt) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      *reinterpret_cast<f32x4*>(dst + 32 * dt + 8 * j) =
-          f32x4{acc[dt][4 * j], acc[dt][4 * j + 1], acc[dt][4 * j + 2], acc[dt][4 * j + 3]};
-    }
+    for (int j = 0; j < 4; ++j)
+      store_grad4(a.dq, dst + 32 * dt + 8 * j, acc[dt][4 * j], acc[dt][4 * j + 1], acc[dt][4 * j + 2], acc[dt][4 * j + 3],
+                  gbf);
   }
 }
 
@@ -345,8 +355,8 @@ void bwd_dkdv_kernel(const BackwardArgs a) {
     if (a.accumulate && key_ok) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const f32x4 x = *reinterpret_cast<const f32x4*>(a.dk + gout + 32 * dt + 8 * j);
-        const f32x4 y = *reinterpret_cast<const f32x4*>(a.dv + gout + 32 * dt + 8 * j);
+        const f32x4 x = *reinterpret_cast<const f32x4*>(static_cast<const float*>(a.dk) + gout + 32 * dt + 8 * j);
+        const f32x4 y = *reinterpret_cast<const f32x4*>(static_cast<const float*>(a.dv) + gout + 32 * dt + 8 * j);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           dk[dt][4 * j + i] = x[i];
@@ -495,14 +505,14 @@ void bwd_dkdv_kernel(const BackwardArgs a) {
   }
 
   if (!key_ok) return;
+  const bool gbf = a.grad_bf16 != 0;
 #pragma unroll
   for (int dt = 0; dt < kDTiles; ++dt) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      *reinterpret_cast<f32x4*>(a.dk + gout + 32 * dt + 8 * j) =
-          f32x4{dk[dt][4 * j], dk[dt][4 * j + 1], dk[dt][4 * j + 2], dk[dt][4 * j + 3]};
-      *reinterpret_cast<f32x4*>(a.dv + gout + 32 * dt + 8 * j) =
-          f32x4{dv[dt][4 * j], dv[dt][4 * j + 1], dv[dt][4 * j + 2], dv[dt][4 * j + 3]};
+      const int64_t e = gout + 32 * dt + 8 * j;
+      store_grad4(a.dk, e, dk[dt][4 * j], dk[dt][4 * j + 1], dk[dt][4 * j + 2], dk[dt][4 * j + 3], gbf);
+      store_grad4(a.dv, e, dv[dt][4 * j], dv[dt][4 * j + 1], dv[dt][4 * j + 2], dv[dt][4 * j + 3], gbf);
     }
   }
 }

@@ -96,9 +96,9 @@ struct BackwardArgs {
   const float* lse;          // forward LSE [B][Sq][Hq], natural log
   const uint16_t* dout;      // gradient of Out, bf16
   float* ws;
-  float* dq;                 // fp32
-  float* dk;                 // fp32; read first when accumulate is set
-  float* dv;
+  void* dq;                  // fp32 or bf16 (grad_bf16)
+  void* dk;                  // fp32 (read first when accumulate is set) or bf16
+  void* dv;
   int64_t q_bstride;
   int64_t kv_bstride;
   int64_t pos0;
@@ -110,6 +110,7 @@ struct BackwardArgs {
   int32_t n_kblocks;         // dK/dV kernel: ceil(kv_len / 128)
   int32_t causal;
   int32_t accumulate;
+  int32_t grad_bf16;         // write dQ/dK/dV as bf16 (RNE of the fp32 result); never with accumulate
   float c;                   // softmax_scale * log2(e), rounded to fp32
   float scale;               // softmax_scale
 };

@@ -208,11 +208,13 @@ rla_status rla_merge_states(const rla_attn_params* p, const rla_partials* parts,
  * k, v [batch][s_max][Hkv][128]; out [batch][q_rows][Hq][128], the forward
  * output in p->out_dtype (bf16 or fp32); lse [batch][q_rows][Hq] fp32, the
  * forward's natural-log LSE.  The gradient reaching LSE is taken as zero.
- * Outputs (device, fp32): dq [batch][q_rows][Hq][128]; dk, dv
- * [batch][s_max][Hkv][128], written for keys [0, cache_len + q_rows) only.
- * accumulate = 0: dk/dv are overwritten.  accumulate = 1: this call's
- * contributions are added to the fp32 values already in dk/dv (which the
- * caller zero-fills before the first call): replaying the query rows as
+ * Outputs (device, grad_dtype: fp32, or bf16 = the round-to-nearest-even of
+ * the fp32 result, the only rounding of the gradients): dq
+ * [batch][q_rows][Hq][128]; dk, dv [batch][s_max][Hkv][128], written for keys
+ * [0, cache_len + q_rows) only.
+ * accumulate = 0: dk/dv are overwritten.  accumulate = 1 (fp32 only): this
+ * call's contributions are added to the fp32 values already in dk/dv (which
+ * the caller zero-fills before the first call): replaying the query rows as
  * consecutive chunks whose cache_len are multiples of 64 gives dq, dk and dv
  * bit for bit equal to one call over all rows.
  * Every element is one fixed-order FP32 MFMA accumulation (dK/dV: query tiles
@@ -225,7 +227,7 @@ rla_status rla_merge_states(const rla_attn_params* p, const rla_partials* parts,
 rla_status rla_attn_backward(const rla_attn_params* p, const void* q, const void* k, const void* v,
                              const void* out, const float* lse, const void* dout, int32_t batch,
                              int32_t q_rows, int32_t cache_len, int32_t s_max, int32_t accumulate,
-                             float* dq, float* dk, float* dv, void* hip_stream);
+                             rla_dtype grad_dtype, void* dq, void* dk, void* dv, void* hip_stream);
 
 /* Selected log-probability through an FP32 lm_head ("WS2 Attention PR5 Drift
  * Benchmark", section "Scope": both attention outputs of a drift comparison go

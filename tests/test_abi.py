@@ -171,8 +171,8 @@ def test_decode_validation_and_workspace(lib):
 def test_backward_rejects_bad_args(lib):
     """The backward entry validates pointers, shapes, the accumulate flag and
     the parameter contract before anything is enqueued."""
-    call = lambda p, b, rows, cache, smax, acc=0, q=FAKE, dq=FAKE: lib.rla_attn_backward(
-        ctypes.byref(p), q, FAKE, FAKE, FAKE, FAKE, FAKE, b, rows, cache, smax, acc, dq, FAKE, FAKE, None)
+    call = lambda p, b, rows, cache, smax, acc=0, q=FAKE, dq=FAKE, gdt=_lib.RLA_DT_FP32: lib.rla_attn_backward(
+        ctypes.byref(p), q, FAKE, FAKE, FAKE, FAKE, FAKE, b, rows, cache, smax, acc, gdt, dq, FAKE, FAKE, None)
     p = _params()
     assert call(p, 1, 16, 0, 16, q=None) == 1
     assert call(p, 1, 16, 0, 16, dq=None) == 1
@@ -181,6 +181,8 @@ def test_backward_rejects_bad_args(lib):
     assert call(p, 1, 16, 8, 16) == 2          # cache_len + q_rows > s_max
     assert call(p, 1, 16, -1, 16) == 2
     assert call(p, 1, 16, 0, 16, acc=2) == 2
+    assert call(p, 1, 16, 0, 16, gdt=7) == 3
+    assert call(p, 1, 16, 0, 16, acc=1, gdt=_lib.RLA_DT_BF16) == 3   # running sums must be fp32
     assert call(_params(head_dim=64), 1, 16, 0, 16) == 3
     assert call(_params(num_kv_heads=5), 1, 16, 0, 16) == 2
     # one head's query rows spanning 2 GiB (Hq=32: 2^18 rows)

@@ -133,6 +133,20 @@ def test_backward_noncausal_replay_bitwise():
     assert_bitwise(dv, ref[2], "non-causal replay dV")
 
 
+def test_backward_bf16_gradients_are_rounded_fp32():
+    """bf16 gradient output is the round-to-nearest-even of the fp32 result,
+    element for element (the downcast is the final write and nothing else)."""
+    B, S, Hq, Hkv = 2, 200, 8, 2
+    q, k, v, do = _inputs(45, B, S, S, Hq, Hkv)
+    qd, kd, vd, dod = dev_bf16(q), dev_bf16(k), dev_bf16(v), dev_bf16(do)
+    out, lse = api.prefill(qd, kd, vd, block=128)
+    g32 = api.backward(qd, kd, vd, out, lse, dod)
+    g16 = api.backward(qd, kd, vd, out, lse, dod, grad_dtype=torch.bfloat16)
+    for a32, a16, n in zip(g32, g16, "qkv"):
+        assert a16.dtype == torch.bfloat16
+        assert_bitwise(a16, a32.to(torch.bfloat16), f"bf16 d{n}")
+
+
 def test_backward_parity_peaky_scores():
     """Large scores (Q and K scaled by 4): probabilities near 0 and 1, where dS
     is most sensitive to the rounding of P."""

@@ -274,13 +274,22 @@ __device__ __forceinline__ int opaque_add(int x, int c) {
 // addr + imm: one register per offset and the immediate offset field,
 // whatever the region's place in LDS (LDS immediates are 16-bit, so a region
 // above 64 KiB would otherwise cost one address add per read).
+// The lane index as a value computed at this point of the program: address
+// arithmetic derived from it is redone where it is used instead of being
+// hoisted out of a loop (where it would hold registers for the whole loop).
+__device__ __forceinline__ int opaque_lane() {
+  int l;
+  asm volatile("v_and_b32 %0, 63, %1" : "=v"(l) : "v"(static_cast<int>(threadIdx.x)));
+  return l;
+}
+
 template <int BK>
 struct KReads {
   const char* reg;
   int ref;
   int a[kDSteps];
-  __device__ __forceinline__ explicit KReads(const char* kreg) : reg(kreg), ref(lds_address(kreg)) {
-    const int lane = threadIdx.x & 63;
+  __device__ __forceinline__ explicit KReads(const char* kreg) : KReads(kreg, static_cast<int>(threadIdx.x & 63)) {}
+  __device__ __forceinline__ KReads(const char* kreg, int lane) : reg(kreg), ref(lds_address(kreg)) {
     const int col = lane & 31;
     const int half = lane >> 5;
 #pragma unroll
@@ -297,15 +306,16 @@ struct VReads {
   const char* reg;
   int ref;
   int a[kDTiles][2];
-  __device__ __forceinline__ explicit VReads(const char* vreg) { init(vreg); }
+  __device__ __forceinline__ explicit VReads(const char* vreg) { init(vreg, static_cast<int>(threadIdx.x & 63)); }
+  __device__ __forceinline__ VReads(const char* vreg, int lane) { init(vreg, lane); }
   __device__ __forceinline__ VReads() {}
   // Bind to a region (at this point of the program, so the address registers
   // live from here on).
-  __device__ __forceinline__ void init(const char* vreg) {
+  __device__ __forceinline__ void init(const char* vreg) { init(vreg, static_cast<int>(threadIdx.x & 63)); }
+  __device__ __forceinline__ void init(const char* vreg, int lane) {
     reg = vreg;
     ref = lds_address(vreg);
     using L = TileLayout<BK>;
-    const int lane = threadIdx.x & 63;
     const int i = lane & 15;
     const int g = lane >> 4;
     const int h = g >> 1;

@@ -3,9 +3,11 @@
 // for the q heads of the group and writes it to the caller's workspace; pass 2
 // (fold.hip) folds the items of each row in ascending block index.  The cut
 // into units is fixed by the lengths alone and never changes what any item
-// holds.  Decode is bound by reading the KV cache, so the next two blocks are
-// kept in flight in registers (K as MFMA A-fragments, V rows bound for LDS)
-// while the current one is computed, and two workgroups share a CU.
+// holds.  Decode is bound by reading the KV cache, so each workgroup keeps two
+// register sets of blocks (K as MFMA A-fragments, V rows bound for LDS) and
+// refills a set with the block two ahead as soon as its registers are free:
+// V right after it is staged in LDS, K right after the score MFMAs have read
+// it.  Two workgroups share a CU.
 //
 // Keys are gathered through the page table: key j of sequence s is slot j % P
 // of page page_table[s][j / P] in a pool laid out [page][kv head][slot][dim].
@@ -65,6 +67,10 @@ struct BlockRegs {
   u32x4 v[VIT];
 
   __device__ __forceinline__ void load(const DecodeArgs& a, const UnitPages& up, int hk, int key0, int len) {
+    load_k(a, up, hk, key0, len);
+    load_v(a, up, hk, key0, len);
+  }
+  __device__ __forceinline__ void load_k(const DecodeArgs& a, const UnitPages& up, int hk, int key0, int len) {
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
     const int lane = tid & 63;
@@ -74,6 +80,9 @@ struct BlockRegs {
 #pragma unroll
       for (int ds = 0; ds < kDSteps; ++ds) k[ds] = gload16(row + 16 * ds);
     }
+  }
+  __device__ __forceinline__ void load_v(const DecodeArgs& a, const UnitPages& up, int hk, int key0, int len) {
+    const int tid = threadIdx.x;
     const int c = tid & 15;
     int64_t off[VIT];
 #pragma unroll
@@ -152,9 +161,9 @@ __device__ __forceinline__ bool locate_unit(const DecodeArgs& a, int64_t u, int&
 // One block's partial states for the group's heads, from the K fragments in
 // registers (waves < NKT) and the V tile in LDS.
 template <int BK, bool F32>
-__device__ __forceinline__ void decode_block(const DecodeArgs& a, char* lds, const BlockRegs<BK>& br,
+__device__ __forceinline__ void decode_block(const DecodeArgs& a, char* lds, BlockRegs<BK>& br,
                                              const bf16x8 (&qf)[kDSteps], int seq, int hk, int64_t blk,
-                                             int64_t len) {
+                                             int64_t len, const UnitPages& up, int next_key0) {
   using Lay = DecodeLds<BK, F32>;
   constexpr int NKT = Lay::NKT;
   const char* lv = lds + Lay::kVOff;  // V rows at lv + TileLayout::v_rel(...)
@@ -173,6 +182,11 @@ __device__ __forceinline__ void decode_block(const DecodeArgs& a, char* lds, con
   if (wave < NKT) {
 #pragma unroll
     for (int ds = 0; ds < kDSteps; ++ds) s = mfma(as_bf16x8(br.k[ds]), qf[ds], s);
+    // K of the block two ahead, into the registers the MFMAs just read (the
+    // fp32-output instance, short of registers, loads it after the block)
+    if constexpr (!F32) {
+      if (next_key0 >= 0) br.load_k(a, up, hk, next_key0, static_cast<int>(len));
+    }
     float m_lane = kNegInf;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
@@ -251,11 +265,14 @@ __device__ __forceinline__ void decode_block(const DecodeArgs& a, char* lds, con
     }
     if (wave == 0 && half == 0) a.items_lse[item] = sc.L;
   }
+  if constexpr (F32) {
+    if (next_key0 >= 0) br.load_k(a, up, hk, next_key0, static_cast<int>(len));
+  }
 }
 
 // Blocks of the unit are processed in pairs so that the two register sets
 // have static indices: while block b is computed, block b+1 is already in
-// registers and block b+2 is being loaded.
+// registers (or in flight) and block b+2 is being loaded into the set of b.
 template <int BK, bool F32>
 __global__ __launch_bounds__(kThreads, 2) void decode_items_kernel(const DecodeArgs a) {
   using Lay = DecodeLds<BK, F32>;
@@ -302,16 +319,18 @@ __global__ __launch_bounds__(kThreads, 2) void decode_items_kernel(const DecodeA
   }
 
   for (int64_t blk = blk0; blk < blk1; blk += 2) {
+    const int n0 = blk + 2 < blk1 ? static_cast<int>((blk + 2) * BK) : -1;
     r0.store_v(lv);
+    if (n0 >= 0) r0.load_v(a, up, hk, n0, ilen);
     lds_barrier();  // V of blk visible
-    decode_block<BK, F32>(a, lds, r0, qf, seq, hk, blk, len);
-    if (blk + 2 < blk1) r0.load(a, up, hk, static_cast<int>((blk + 2) * BK), ilen);
+    decode_block<BK, F32>(a, lds, r0, qf, seq, hk, blk, len, up, n0);
     lds_barrier();  // everyone done with V / P of blk
     if (blk + 1 < blk1) {
+      const int n1 = blk + 3 < blk1 ? static_cast<int>((blk + 3) * BK) : -1;
       r1.store_v(lv);
+      if (n1 >= 0) r1.load_v(a, up, hk, n1, ilen);
       lds_barrier();
-      decode_block<BK, F32>(a, lds, r1, qf, seq, hk, blk + 1, len);
-      if (blk + 3 < blk1) r1.load(a, up, hk, static_cast<int>((blk + 3) * BK), ilen);
+      decode_block<BK, F32>(a, lds, r1, qf, seq, hk, blk + 1, len, up, n1);
       lds_barrier();
     }
   }

@@ -10,7 +10,7 @@ namespace rla {
 
 constexpr int kHeadDimPublic = 128;  // the only head dimension the kernels implement
 constexpr int kMaxParts = 512;  // partial states per merge / owned blocks per emit launch
-constexpr int kDecodeUnitBlocks = 8;  // KV blocks one decode workgroup walks
+constexpr int kDecodeUnitBlocks = 4;  // KV blocks one decode workgroup walks
 
 // Prefill and chunked prefill.  Query row t of batch b sits at absolute
 // position pos0 + t; it attends keys [0, kv_len) (and key <= position when

@@ -578,8 +578,8 @@ def summarize_profiles(d):
                      for m in ("prefill", "decode", "copy"))
 
     # prefill
-    st = stats_rows("prefill", ["prefill_pipe_kernel"])
-    fk, wk, fb, wb, n = counters("prefill", "prefill_pipe_kernel")
+    st = stats_rows("prefill", ["prefill_pp_kernel"])
+    fk, wk, fb, wb, n = counters("prefill", "prefill_pp_kernel")
     name, calls, avg, mn, mx = st[0]
     flops = cfg.flops()
     lines = [

@@ -66,16 +66,21 @@ def test_ragged_multi_tile(block, out_dtype):
     _run_and_check(q, k, v, block=block, out_dtype=out_dtype, what="ragged multi-tile")
 
 
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])
 @pytest.mark.parametrize("Hq,Hkv", [(4, 4), (4, 2), (16, 2)], ids=["mha", "gqa2", "gqa8"])
-def test_group_sizes(Hq, Hkv):
-    """GQA groups other than 4 (MHA, 2, 8) map heads to kv heads correctly."""
+def test_group_sizes(Hq, Hkv, out_dtype):
+    """GQA groups other than 4 (MHA, 2, 8) map heads to kv heads correctly (the
+    workgroup then holds 8 position groups of one head, 4 of two heads, or one
+    of eight heads)."""
     q, k, v = _rand(4, (1, 200, Hq, 128)), _rand(5, (1, 200, Hkv, 128)), _rand(6, (1, 200, Hkv, 128))
-    _run_and_check(q, k, v, block=128, out_dtype=torch.float32, what=f"group Hq={Hq} Hkv={Hkv}")
+    _run_and_check(q, k, v, block=128, out_dtype=out_dtype, what=f"group Hq={Hq} Hkv={Hkv}")
 
 
-def test_non_causal():
+@pytest.mark.parametrize("block", [64, 128])
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])
+def test_non_causal(block, out_dtype):
     q, k, v = _rand(7, (1, 150, 8, 128)), _rand(8, (1, 150, 2, 128)), _rand(9, (1, 150, 2, 128))
-    _run_and_check(q, k, v, block=64, out_dtype=torch.float32, causal=False, what="non-causal")
+    _run_and_check(q, k, v, block=block, out_dtype=out_dtype, causal=False, what="non-causal")
 
 
 def test_peaky_scores():

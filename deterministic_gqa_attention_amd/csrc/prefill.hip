@@ -565,9 +565,10 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe_kernel(const PrefillArg
 // the buffer of K_{j-1}); K and V are double-buffered and Q stays in
 // registers.  Only group 0 issues the loads, and always into the kind of
 // buffer (K or V) it is not reading in that half-step, so no LDS read of
-// either group waits for a load in flight.  Per block and wave the operations are those of the other fused
-// kernels (block_scores, block_softmax, fold_prepare, block_pv_fold), so the
-// result is the same bits.
+// either group waits for a load in flight.  Per block and wave the
+// operations are those of the other fused kernels (block_scores,
+// block_softmax, fold_prepare, block_pv_fold), so the result is the same
+// bits.
 template <int BK>
 __global__ __launch_bounds__(kThreads) void prefill_pp_kernel(const PrefillArgs a) {
   using L = TileLayout<BK>;
@@ -613,14 +614,15 @@ __global__ __launch_bounds__(kThreads) void prefill_pp_kernel(const PrefillArgs 
     wait_direct_loads();
     lds_barrier();
   };
-  // The stages.  The buffer read and the buffer being filled in the same
-  // half-step are restrict pointers, so the compiler does not make the reads
-  // wait for the loads.
+  // The stages.  The regions are passed as restrict pointers into separate K
+  // and V arrays, which lets the compiler's wait insertion see that a stage's
+  // LDS reads do not touch the region group 0 is loading.
   auto scores_half = [&](int64_t j, const char* __restrict__ kc, f32x16 (&s)[BK / 32]) {
     if (wave_sees<BK>(a, tm, j)) block_scores<BK>(kc, w.qf, s, opaque_lane());
   };
   // The vector stage is the longer of the two, so its wave gets the higher
-  // issue priority while it runs (measured: 2-4 % faster than equal priority).
+  // issue priority while it runs (measured: about 2 % faster than equal
+  // priority).
   auto vector_half = [&](int64_t j, const char* __restrict__ vc, f32x16 (&s)[BK / 32]) {
     if (!wave_sees<BK>(a, tm, j)) return;
     __builtin_amdgcn_s_setprio(2);

@@ -62,6 +62,9 @@ PMC_CMD = ("rocprofv3 --pmc {c} -d gpurun_out/pmc_{c}_{m} -o run --output-format
            "python3 bench.py --only {m} --steps 2 --warmup 1 --decode-steps 2")
 PMC_CMD_LM_HEAD = ("rocprofv3 --pmc {c} -d gpurun_out/pmc_{c}_lm_head -o run --output-format csv -- "
                    "python3 bench.py --only lm_head")
+PMC_CMD_MFMA = ("rocprofv3 --pmc GRBM_GUI_ACTIVE SQ_BUSY_CYCLES SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU SQ_INSTS_MFMA "
+                "SQ_WAVE_CYCLES -d gpurun_out/pmc_mfma_prefill -o run --output-format csv -- "
+                "python3 bench.py --only prefill --steps 2 --warmup 1")
 PMC_CMD_BACKWARD = ("rocprofv3 --pmc {c} -d gpurun_out/pmc_{c}_backward -o run --output-format csv -- "
                     "python3 bench.py --only backward --steps 2")
 
@@ -661,6 +664,56 @@ def summarize_profiles(d):
         summarize_backward(d, f_fetch, f_write, header, src)
     if os.path.isdir(os.path.join(d, "prof_lm_head")):
         summarize_lm_head(d, f_fetch, f_write, header, src)
+    if os.path.isdir(os.path.join(d, "pmc_mfma_prefill")):
+        summarize_mfma(d, src)
+
+
+def summarize_mfma(d, src):
+    """profiles/prefill_mfma_counters_b4_s4096.md: clock, MFMA and VALU activity
+    of the bf16 prefill kernel from one counter run (per-XCD GRBM counters are
+    summed by rocprofv3, so the busy cycles of one XCD are the sum / 8)."""
+    rows = _read_csv(os.path.join(d, "pmc_mfma_prefill", "run_counter_collection.csv"))
+    per = {}
+    for r in rows:
+        if "prefill_pp_kernel" not in r["Kernel_Name"]:
+            continue
+        e = per.setdefault(r["Dispatch_Id"], {"_ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
+        e[r["Counter_Name"]] = e.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    runs = list(per.values())
+    mean = {k: float(np.mean([x[k] for x in runs])) for k in runs[0]}
+    cfg = gen.CFG2
+    n_xcd, n_simd = 8, 1024
+    clk = mean["GRBM_GUI_ACTIVE"] / n_xcd / mean["_ns"]  # GHz
+    busy = mean["GRBM_GUI_ACTIVE"] / n_xcd
+    mfma_flop = mean["SQ_INSTS_MFMA"] * 32 * 32 * 16 * 2
+    lines = [
+        "# Prefill kernel MFMA and VALU counters, causal B=4 S=4096 Hq=32 Hkv=8 D=128, bf16 out",
+        "",
+        "    " + PMC_CMD_MFMA,
+        "",
+        f"Mean over {len(runs)} dispatches of `prefill_pp_kernel<128>`:",
+        "",
+        "| counter | value per dispatch |",
+        "|---|---|",
+    ] + [f"| {k} | {v:.0f} |" for k, v in sorted(mean.items()) if not k.startswith("_")] + [
+        f"| duration (ns) | {mean['_ns']:.0f} |",
+        "",
+        f"* Clock: GRBM_GUI_ACTIVE / 8 XCDs / duration = {clk:.2f} GHz.",
+        f"* MFMA instructions (v_mfma_f32_32x32x16_bf16, 32768 flop each): {mean['SQ_INSTS_MFMA']:.0f} = "
+        f"{mfma_flop:.4e} flop executed, {mfma_flop / cfg.flops():.3f} x the algorithmic {cfg.flops():.4e} "
+        "(the masked halves of diagonal blocks).",
+        f"* Matrix-core busy: SQ_VALU_MFMA_BUSY_CYCLES / (busy cycles x {n_simd} SIMDs) = "
+        f"{mean['SQ_VALU_MFMA_BUSY_CYCLES'] / (busy * n_simd):.3f}.",
+        f"* VALU instructions (MFMAs included): {mean['SQ_INSTS_VALU']:.0f}, "
+        f"{mean['SQ_INSTS_VALU'] * 4 / (busy * n_simd):.3f} of the SIMDs' cycles at 4 cycles per wave64 instruction.",
+        "",
+        f"kernel source sha256: `{src}`",
+        "",
+    ]
+    path = os.path.join(PROFILES, "prefill_mfma_counters_b4_s4096.md")
+    with open(path, "w") as f:
+        f.write("\n".join(lines))
+    print(f"wrote {path}")
 
 
 def summarize_lm_head(d, f_fetch, f_write, header, src):

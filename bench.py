@@ -303,7 +303,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-reported", action="store_true", help="skip the long-context and chunked-replay legs")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--only", choices=["prefill", "decode", "copy", "backward", "lm_head"], default=None,
                     help="run one leg only (for profiler and counter runs)")
     ap.add_argument("--summarize", metavar="DIR", default=None,

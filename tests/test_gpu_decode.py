@@ -96,6 +96,40 @@ def test_decode_equals_prefill_last_row():
         assert_bitwise(dl[s], pl[0, L - 1], f"seq {s} LSE")
 
 
+# Lengths around the boundaries of the decode workgroup units (4 KV blocks:
+# 512 keys at 128-key blocks, 256 at 64): a sequence's last unit then holds
+# 1, 2, 3 or 4 blocks, with or without a block two ahead to prefetch.
+UNIT_LENS = np.array([255, 256, 257, 511, 512, 513, 640, 769, 1023, 1024, 1025, 1537, 2049, 2303], np.int32)
+UNITS = gen.DecodeConfig(43, "decode unit boundaries", batch=len(UNIT_LENS), Hq=8, Hkv=2, D=128, page_size=16,
+                         num_pages=1024, len_lo=1, len_hi=2400, block=128)
+
+
+@pytest.mark.parametrize("block", [64, 128])
+def test_unit_boundaries_parity_and_prefill_identity(block):
+    """Decode at lengths around the unit boundaries matches the oracle, and
+    every sequence's Out/LSE equal the last row of a causal prefill over the
+    same tokens, bitwise."""
+    cfg = dataclasses.replace(UNITS, block=block)
+    d = gen.decode_inputs(cfg, lengths=UNIT_LENS)
+    say(f"[decode] unit boundaries block={block}")
+    do, dl = _decode(d, cfg, block=block, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ro, rl = oracle.decode_paged(d["q"], d["k_pool"], d["v_pool"], d["page_table"], d["ctx_lens"],
+                                 scale=cfg.softmax_scale)
+    stats = check_parity(host_f64(do), host_f64(dl), ro, rl, f32_out=True, what="unit-boundary decode")
+    say(f"    parity {stats}")
+    P = cfg.page_size
+    for s, L in enumerate(UNIT_LENS.tolist()):
+        pages = d["page_table"][s, : -(-L // P)]
+        k = d["k_pool"][pages].transpose(0, 2, 1, 3).reshape(-1, cfg.Hkv, 128)[:L][None]
+        v = d["v_pool"][pages].transpose(0, 2, 1, 3).reshape(-1, cfg.Hkv, 128)[:L][None]
+        q = np.zeros((1, L, cfg.Hq, 128), np.uint16)
+        q[0, L - 1] = d["q"][s]
+        po, pl = api.prefill(dev_bf16(q), dev_bf16(k), dev_bf16(v), block=block, out_dtype=torch.float32)
+        assert_bitwise(do[s], po[0, L - 1], f"len {L} Out")
+        assert_bitwise(dl[s], pl[0, L - 1], f"len {L} LSE")
+
+
 @pytest.mark.parametrize("block,pages", [(128, (1, 2, 4, 8, 32, 64, 128)), (64, (1, 8, 32, 64))])
 def test_page_sizes_bitwise(block, pages):
     """The page size only changes where keys live: every page size that

@@ -28,6 +28,8 @@
 // LDS read on the in-flight loads (it would otherwise wait for every
 // outstanding direct load before the first read).  No atomics and no split
 // of a block across workgroups, so nothing depends on scheduling.
+#include <type_traits>
+
 #include "kernels.hpp"
 #include "tile.hpp"
 
@@ -550,39 +552,44 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe_kernel(const PrefillArg
 }
 
 // bf16 output, ping-pong schedule.  Waves w and w+4 of the workgroup share a
-// SIMD; the two halves of the workgroup (waves 0-3 and 4-7) run the same
-// per-block work offset by one stage, so on every SIMD one wave computes
-// scores (matrix cores only) while the other runs the softmax, PV and fold of
-// a block (vector ALU, with its own PV MFMAs), and the two kinds of work
-// overlap instead of taking turns.  Time is cut into half-steps, each ended
-// by a workgroup barrier; in half-step h a wave of group g (0 or 1) is at
-// stage h - g of its own sequence
-//   stage 2j:   S_j = K_j Q^T
-//   stage 2j+1: softmax of S_j, PV of block j and its fold
-// so K_j is read in half-steps 2j and 2j+1 and V_j in 2j+1 and 2j+2.  Each
-// half-step loads what the next one needs and waits for it at its end:
-// V_j in half-step 2j (into the buffer V_{j-2} left), K_{j+1} in 2j+1 (into
-// the buffer of K_{j-1}); K and V are double-buffered and Q stays in
-// registers.  Only group 0 issues the loads, and always into the kind of
-// buffer (K or V) it is not reading in that half-step, so no LDS read of
-// either group waits for a load in flight.  Per block and wave the
-// operations are those of the other fused kernels (block_scores,
-// block_softmax, fold_prepare, block_pv_fold), so the result is the same
-// bits.
+// SIMD.  Each wave's work is cut into two kinds of stage that use different
+// units:
+//   matrix stage A_j: PV of block j-1 with its fold (block_pv_fold), then
+//                     S_j = K_j Q^T (block_scores)  -- 64 MFMAs and the fold
+//   vector stage B_j: the softmax of S_j (block_softmax, fold_prepare)
+// and a wave runs A_0, B_0, A_1, B_1, ..., A_n (n blocks; A_0 has no PV, A_n
+// no scores).  The two halves of the workgroup (waves 0-3 and 4-7) run this
+// sequence one stage apart: time is cut into half-steps ended by a workgroup
+// barrier, and in half-step h a wave of group g is at stage h - g, so on
+// every SIMD one wave issues matrix work while the other issues vector work.
+// K_j is read in half-steps 2j (group 0) and 2j+1 (group 1), V_j in 2j+2 and
+// 2j+3.  Group 1 issues all loads, at the start of each of its vector stages
+// (which read no LDS): in half-step 2i it loads K_{i+1} and V_i, and it waits
+// for them at the end of half-step 2i+1, so every load has two half-steps to
+// land.  K and V are double-buffered in four separate LDS arrays, and the
+// block loop is unrolled by two so that each stage names its arrays at
+// compile time: the compiler then sees that the matrix stage's fragment reads
+// and the loads in flight touch different arrays, and does not make the
+// reads wait.  Q stays in registers.  Per block and wave the operations are
+// those of the other fused kernels, so the result is the same bits.
 template <int BK>
 __global__ __launch_bounds__(kThreads) void prefill_pp_kernel(const PrefillArgs a) {
   using L = TileLayout<BK>;
-  using Ld = BlockLoader<BK, kWaves / 2>;  // the waves of group 0
+  using Ld = BlockLoader<BK, kWaves / 2>;  // the waves of group 1
   using P = BlockP<BK, false>;
-  __shared__ __attribute__((aligned(16))) char kbuf[2 * L::kKBytes];
-  __shared__ __attribute__((aligned(16))) char vbuf[2 * L::kVBytes];
+  constexpr int NKT = BK / 32;
+  __shared__ __attribute__((aligned(16))) char kb0[L::kKBytes];
+  __shared__ __attribute__((aligned(16))) char kb1[L::kKBytes];
+  __shared__ __attribute__((aligned(16))) char vb0[L::kVBytes];
+  __shared__ __attribute__((aligned(16))) char vb1[L::kVBytes];
 
   WaveCtx w;
   wave_setup(a, blockIdx.x, w);
   const TileMap& tm = w.tm;
   const int64_t n_kv_blocks = (a.kv_len + BK - 1) / BK;
   const int64_t nblk = a.causal ? min(n_kv_blocks, (a.pos0 + tm.tile_t1) / BK + 1) : n_kv_blocks;
-  const int group = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6)) >> 2;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  const int group = wave >> 2;
 
   FoldState fs{kNegInf, 0.0f};
   f32x16 acc[kDTiles];
@@ -591,69 +598,143 @@ __global__ __launch_bounds__(kThreads) void prefill_pp_kernel(const PrefillArgs 
 
   sched_fence();  // the Q loads of wave_setup stay ahead of the direct loads
   Ld ld;
-  ld.init(static_cast<int>(w.row_stride));
-  if (group == 0 && nblk > 0) ld.issue_k(kbuf, w.krs, 0);
-  wait_direct_loads();  // Q, K_0
-  lds_barrier();
+  ld.init(static_cast<int>(w.row_stride), wave & 3);
 
   const int kvl = static_cast<int>(a.kv_len);
   const int qpos = static_cast<int>(tm.qpos);
-  auto kreg = [&](int64_t j) { return kbuf + static_cast<int>(j & 1) * L::kKBytes; };
-  auto vreg = [&](int64_t j) { return vbuf + static_cast<int>(j & 1) * L::kVBytes; };
-  // Loads of a half-step (group 0): V_j (even half-step 2j) or K_j (odd
-  // half-step 2j-1), when block j exists.
-  auto issue_v = [&](int64_t j, char* __restrict__ dst) {
-    if (j < nblk) ld.issue_v(dst, w.vrs, j * BK);
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+
+  // Loads of half-step 2i (group 1): K_{i+1} into the K array of parity
+  // (i+1)&1 and V_i into the V array of parity i&1.  par = i & 1.
+  auto loads = [&](auto par, int64_t i) {
+    constexpr int p = decltype(par)::value;
+    if (i + 1 < nblk) ld.issue_k(p ? kb0 : kb1, w.krs, (i + 1) * BK);
+    if (i < nblk) ld.issue_v(p ? vb1 : vb0, w.vrs, i * BK);
   };
-  auto issue_k = [&](int64_t j, char* __restrict__ dst) {
-    if (j < nblk) ld.issue_k(dst, w.krs, j * BK);
+  // Matrix stage A_j (par = j & 1): PV + fold of block j-1 from the V array of
+  // parity (j-1)&1, then the scores of block j from the K array of parity j&1.
+  // The matrix stage is the one the SIMD's throughput depends on, so its wave
+  // gets the higher issue priority.
+  auto stage_a = [&](auto par, int64_t j, f32x16 (&s)[NKT], const P& pp, const FoldIn& inp) {
+    constexpr int p = decltype(par)::value;
+    const char* kc = p ? kb1 : kb0;
+    const char* vp = p ? vb0 : vb1;
+    __builtin_amdgcn_s_setprio(2);
+    if (j > 0 && wave_sees<BK>(a, tm, j - 1)) block_pv_fold<BK, false>(VReads<BK>(vp, opaque_lane()), pp, inp, acc);
+    sched_fence();
+    if (j < nblk && wave_sees<BK>(a, tm, j)) {
+      block_scores<BK>(kc, w.qf, s, opaque_lane());
+    } else {
+#pragma unroll
+      for (int kt = 0; kt < NKT; ++kt) s[kt] = f32x16{};  // defined on every path (unused)
+    }
+    __builtin_amdgcn_s_setprio(0);
   };
-  // End of a half-step: its loads have landed, then the barrier.
+  // Vector stage B_j: softmax of S_j, fold scalars of block j.
+  auto stage_b = [&](int64_t j, f32x16 (&s)[NKT], P& pn, FoldIn& inn) {
+    if (!wave_sees<BK>(a, tm, j)) {
+      pn = P{};  // defined on every path, so the previous block's P is dead after its PV
+      inn = FoldIn{};
+      return;
+    }
+    block_softmax<BK, false>(s, !wave_full<BK>(a, tm, j), static_cast<int>(j * BK), kvl, a.causal, qpos, a.c, pn);
+    inn = fold_prepare(fs, pn.m_t, pn.l_b);
+  };
+  // End of a half-step: (group 1, when it has loads in flight) wait for
+  // them, then the barrier.
   auto end_half = [&]() {
+    sched_fence();
+    lds_barrier();
+  };
+  auto end_half_wait = [&]() {
     sched_fence();
     wait_direct_loads();
     lds_barrier();
   };
-  // The stages.  The regions are passed as restrict pointers into separate K
-  // and V arrays, which lets the compiler's wait insertion see that a stage's
-  // LDS reads do not touch the region group 0 is loading.
-  auto scores_half = [&](int64_t j, const char* __restrict__ kc, f32x16 (&s)[BK / 32]) {
-    if (wave_sees<BK>(a, tm, j)) block_scores<BK>(kc, w.qf, s, opaque_lane());
-  };
-  // The vector stage is the longer of the two, so its wave gets the higher
-  // issue priority while it runs (measured: about 2 % faster than equal
-  // priority).
-  auto vector_half = [&](int64_t j, const char* __restrict__ vc, f32x16 (&s)[BK / 32]) {
-    if (!wave_sees<BK>(a, tm, j)) return;
-    __builtin_amdgcn_s_setprio(2);
-    P p;
-    block_softmax<BK, false>(s, !wave_full<BK>(a, tm, j), static_cast<int>(j * BK), kvl, a.causal, qpos, a.c, p);
-    const FoldIn in = fold_prepare(fs, p.m_t, p.l_b);
-    block_pv_fold<BK, false>(VReads<BK>(vc, opaque_lane()), p, in, acc);
-    __builtin_amdgcn_s_setprio(0);
-  };
-  // Both groups run the same 2*nblk + 1 half-steps (and barriers); the loop
-  // is written once per group so that the scores of a block are live only
-  // from its scores stage to its vector stage.
+
+  P pb{};        // softmax result of the block whose PV is pending
+  FoldIn ib{};   // and its fold scalars
   if (group == 0) {
-    for (int64_t j = 0; j < nblk; ++j) {
-      f32x16 s[BK / 32];
-      issue_v(j, vreg(j));  // half-step 2j
-      scores_half(j, kreg(j), s);
+    lds_barrier();  // prologue: K_0 landed
+    int64_t j = 0;
+    for (; j + 2 <= nblk; j += 2) {
+      {
+        f32x16 s[NKT];
+        stage_a(I0{}, j, s, pb, ib);  // half-step 2j
+        end_half();
+        stage_b(j, s, pb, ib);        // 2j+1
+        end_half();
+      }
+      {
+        f32x16 s[NKT];
+        stage_a(I1{}, j + 1, s, pb, ib);
+        end_half();
+        stage_b(j + 1, s, pb, ib);
+        end_half();
+      }
+    }
+    if (j < nblk) {
+      f32x16 s[NKT];
+      stage_a(I0{}, j, s, pb, ib);
       end_half();
-      issue_k(j + 1, kreg(j + 1));  // half-step 2j+1
-      vector_half(j, vreg(j), s);
+      stage_b(j, s, pb, ib);
       end_half();
     }
-    end_half();  // half-step 2*nblk
+    {
+      f32x16 s[NKT];
+      if (nblk & 1) {
+        stage_a(I1{}, nblk, s, pb, ib);  // half-step 2n: PV of the last block
+      } else {
+        stage_a(I0{}, nblk, s, pb, ib);
+      }
+      end_half();
+    }
+    end_half();  // half-step 2n+1
   } else {
+    // prologue: K_0 (and the Q rows) landed; then the loads of half-step 0
+    // (K_1, V_0), with nothing else in flight, so the compiler's wait
+    // counting stays exact
+    if (nblk > 0) ld.issue_k(kb0, w.krs, 0);
+    wait_direct_loads();
+    lds_barrier();
+    loads(I0{}, 0);
     end_half();  // half-step 0
-    for (int64_t j = 0; j < nblk; ++j) {
-      f32x16 s[BK / 32];
-      scores_half(j, kreg(j), s);  // half-step 2j+1
+    int64_t j = 0;
+    for (; j + 2 <= nblk; j += 2) {
+      {
+        f32x16 s[NKT];
+        stage_a(I0{}, j, s, pb, ib);  // half-step 2j+1
+        end_half_wait();
+        loads(I1{}, j + 1);           // half-step 2j+2
+        stage_b(j, s, pb, ib);
+        end_half();
+      }
+      {
+        f32x16 s[NKT];
+        stage_a(I1{}, j + 1, s, pb, ib);
+        end_half_wait();
+        loads(I0{}, j + 2);
+        stage_b(j + 1, s, pb, ib);
+        end_half();
+      }
+    }
+    if (j < nblk) {
+      f32x16 s[NKT];
+      stage_a(I0{}, j, s, pb, ib);
+      end_half_wait();
+      loads(I1{}, j + 1);
+      stage_b(j, s, pb, ib);
       end_half();
-      vector_half(j, vreg(j), s);  // half-step 2j+2
-      end_half();
+    }
+    {
+      f32x16 s[NKT];
+      if (nblk & 1) {
+        stage_a(I1{}, nblk, s, pb, ib);  // half-step 2n+1
+      } else {
+        stage_a(I0{}, nblk, s, pb, ib);
+      }
+      end_half_wait();
     }
   }
 

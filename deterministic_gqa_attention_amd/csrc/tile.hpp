@@ -80,7 +80,12 @@ struct BlockLoader {
   int row_bytes;
 
   __device__ __forceinline__ void init(int row_stride) {
-    wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+    init(row_stride, __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6)));
+  }
+  // The same for a loading team of NW waves whose member index (0..NW-1) is
+  // w, e.g. the upper half of a workgroup.
+  __device__ __forceinline__ void init(int row_stride, int w) {
+    wave = w;
     row_bytes = row_stride * 2;
     const int lane = threadIdx.x & 63;
     const int p = lane & 15;

@@ -21,6 +21,7 @@ RLA_MAX_PARTS = 512
 # Every function include/rla_attn.h declares.
 EXPORTS = ("rla_attn_prefill", "rla_attn_prefill_chunked", "rla_attn_prefill_paged", "rla_attn_decode_paged",
            "rla_merge_states", "rla_attn_backward", "rla_lm_head_logprobs", "rla_decode_workspace_bytes",
+           "rla_chunked_workspace_bytes", "rla_backward_workspace_bytes", "rla_lm_head_workspace_bytes",
            "rla_last_error", "rla_core_id")
 
 
@@ -66,21 +67,28 @@ def load(path: str = LIB_PATH):
     pp = ctypes.POINTER(RlaParams)
     lib.rla_attn_prefill.argtypes = [pp, P, P, P, i32, i32, ctypes.POINTER(RlaShard), P, P, P]
     lib.rla_attn_prefill.restype = ctypes.c_int
-    lib.rla_attn_prefill_chunked.argtypes = [pp, P, P, P, i32, i32, i32, i32, ctypes.POINTER(RlaShard), P, P, P]
+    lib.rla_attn_prefill_chunked.argtypes = [pp, P, P, P, i32, i32, i32, i32, ctypes.POINTER(RlaShard), P, sz, P, P,
+                                             P]
     lib.rla_attn_prefill_chunked.restype = ctypes.c_int
     lib.rla_attn_prefill_paged.argtypes = [pp, P, P, P, i64, i32, P, i32, i32, i32, i32, P, P, P]
     lib.rla_attn_prefill_paged.restype = ctypes.c_int
     lib.rla_attn_decode_paged.argtypes = [pp, P, P, P, i64, i32, P, i32, P, ctypes.POINTER(ctypes.c_int32),
                                           i32, i32, P, sz, P, P, P]
     lib.rla_attn_decode_paged.restype = ctypes.c_int
-    lib.rla_attn_backward.argtypes = [pp, P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, P, P, P, P]
+    lib.rla_attn_backward.argtypes = [pp, P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, P, P, P, P, sz, P]
     lib.rla_attn_backward.restype = ctypes.c_int
-    lib.rla_lm_head_logprobs.argtypes = [P, i32, P, P, i32, i32, i32, P, P, P]
+    lib.rla_lm_head_logprobs.argtypes = [P, i32, P, P, i32, i32, i32, P, P, P, sz, P]
     lib.rla_lm_head_logprobs.restype = ctypes.c_int
     lib.rla_merge_states.argtypes = [pp, ctypes.POINTER(RlaPartials), P, P, P]
     lib.rla_merge_states.restype = ctypes.c_int
     lib.rla_decode_workspace_bytes.argtypes = [pp, i32, i32]
     lib.rla_decode_workspace_bytes.restype = sz
+    lib.rla_chunked_workspace_bytes.argtypes = [pp, i32, i32, i32, i32]
+    lib.rla_chunked_workspace_bytes.restype = sz
+    lib.rla_backward_workspace_bytes.argtypes = [pp, i32, i32]
+    lib.rla_backward_workspace_bytes.restype = sz
+    lib.rla_lm_head_workspace_bytes.argtypes = [i32, i32]
+    lib.rla_lm_head_workspace_bytes.restype = sz
     lib.rla_last_error.argtypes = []
     lib.rla_last_error.restype = ctypes.c_char_p
     lib.rla_core_id.argtypes = []

@@ -12,11 +12,12 @@ import math
 
 import torch
 
-from . import _lib
+from . import _checks, _lib
 from ._lib import RLAError, RlaParams, RlaPartials, RlaShard
 
 __all__ = ["RLAError", "core_id", "prefill", "prefill_chunked", "prefill_paged", "emit_partials",
-           "merge_states", "decode_paged", "decode_workspace_bytes", "backward", "lm_head_logprobs", "params"]
+           "merge_states", "decode_paged", "decode_workspace_bytes", "backward", "lm_head_logprobs", "params",
+           "alloc_workspace"]
 
 _OUT_DT = {torch.bfloat16: _lib.RLA_DT_BF16, torch.float32: _lib.RLA_DT_FP32}
 _ORDER = {"global_block_index": _lib.RLA_ORDER_GLOBAL_BLOCK_INDEX, "arrival": _lib.RLA_ORDER_ARRIVAL}
@@ -58,6 +59,27 @@ def _stream(device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
 
+def _same_device(*tensors) -> None:
+    devs = {t.device for t in tensors if t is not None}
+    if len(devs) > 1:
+        raise ValueError(f"tensors live on different devices: {sorted(str(d) for d in devs)}")
+
+
+def alloc_workspace(nbytes: int, device) -> torch.Tensor:
+    """Device scratch of at least ``nbytes`` for an entry point's workspace argument."""
+    return torch.empty((max(int(nbytes), 1),), dtype=torch.uint8, device=device)
+
+
+def _ws(buf, need: int, device):
+    """(pointer, bytes) of a caller-given or freshly allocated workspace."""
+    if need <= 0 and buf is None:
+        return None, 0
+    if buf is None:
+        buf = alloc_workspace(need, device)
+    _dev(buf, "workspace")
+    return buf, buf.numel() * buf.element_size()
+
+
 def _i64_array(values):
     vals = [int(x) for x in values]
     return (ctypes.c_int64 * len(vals))(*vals), len(vals)
@@ -75,8 +97,9 @@ def _shard_struct(kv_blocks, q_begin, q_count, part_out, part_lse, rows):
 def prefill(q, k, v, *, block, out_dtype=torch.bfloat16, causal=True, scale=None):
     """Fused causal prefill.  q [B,S,Hq,128], k/v [B,S,Hkv,128] bf16 ->
     (out [B,S,Hq,128] out_dtype, lse [B,S,Hq] fp32)."""
-    B, S, Hq, D = q.shape
-    Hkv = k.shape[2]
+    B, S, Hq, Hkv = _checks.prefill(q.shape, k.shape, v.shape)
+    _same_device(q, k, v)
+    D = q.shape[3]
     p = params(Hq, Hkv, block=block, out_dtype=out_dtype, causal=causal, scale=scale, head_dim=D)
     out = torch.empty((B, S, Hq, D), dtype=out_dtype, device=q.device)
     lse = torch.empty((B, S, Hq), dtype=torch.float32, device=q.device)
@@ -88,19 +111,23 @@ def prefill(q, k, v, *, block, out_dtype=torch.bfloat16, causal=True, scale=None
 
 
 def prefill_chunked(q_chunk, k_cache, v_cache, *, cache_len, block, out_dtype=torch.bfloat16, causal=True,
-                    scale=None):
+                    scale=None, workspace=None):
     """One chunked-prefill replay step.  q_chunk [B,C,Hq,128]; caches
-    [B,S_max,Hkv,128] already holding the chunk's K/V -> (out, lse)."""
-    B, C, Hq, D = q_chunk.shape
-    S_max, Hkv = k_cache.shape[1], k_cache.shape[2]
+    [B,S_max,Hkv,128] already holding the chunk's K/V -> (out, lse).  A chunk of
+    one query uses a device workspace (allocated here unless given)."""
+    B, C, Hq, Hkv, S_max = _checks.chunked(q_chunk.shape, k_cache.shape, v_cache.shape, int(cache_len))
+    _same_device(q_chunk, k_cache, v_cache, workspace)
+    D = q_chunk.shape[3]
     p = params(Hq, Hkv, block=block, out_dtype=out_dtype, causal=causal, scale=scale, head_dim=D)
     out = torch.empty((B, C, Hq, D), dtype=out_dtype, device=q_chunk.device)
     lse = torch.empty((B, C, Hq), dtype=torch.float32, device=q_chunk.device)
     lib = _lib.load()
+    need = int(lib.rla_chunked_workspace_bytes(ctypes.byref(p), B, C, int(cache_len), S_max))
+    ws, ws_bytes = _ws(workspace, need, q_chunk.device)
     _lib.check(lib.rla_attn_prefill_chunked(
         ctypes.byref(p), _dev(q_chunk, "q_chunk", torch.bfloat16, 4), _dev(k_cache, "k_cache", torch.bfloat16, 4),
-        _dev(v_cache, "v_cache", torch.bfloat16, 4), B, C, int(cache_len), S_max, None, out.data_ptr(),
-        lse.data_ptr(), _stream(q_chunk.device)))
+        _dev(v_cache, "v_cache", torch.bfloat16, 4), B, C, int(cache_len), S_max, None,
+        None if ws is None else ws.data_ptr(), ws_bytes, out.data_ptr(), lse.data_ptr(), _stream(q_chunk.device)))
     return out, lse
 
 
@@ -109,8 +136,10 @@ def prefill_paged(q_chunk, k_pool, v_pool, page_table, *, cache_len, block, out_
     """Chunked prefill over paged pools.  q_chunk [B,C,Hq,128]; pools
     [num_pages,Hkv,P,128] bf16 already holding the chunk's K/V; page_table
     [B,max_pages] int32 -> (out, lse)."""
-    B, C, Hq, D = q_chunk.shape
-    num_pages, Hkv, P, _ = k_pool.shape
+    B, C, Hq, Hkv, num_pages, P, _ = _checks.paged(q_chunk.shape, k_pool.shape, v_pool.shape, page_table.shape,
+                                                   int(cache_len))
+    _same_device(q_chunk, k_pool, v_pool, page_table)
+    D = q_chunk.shape[3]
     p = params(Hq, Hkv, block=block, out_dtype=out_dtype, causal=causal, scale=scale, head_dim=D)
     out = torch.empty((B, C, Hq, D), dtype=out_dtype, device=q_chunk.device)
     lse = torch.empty((B, C, Hq), dtype=torch.float32, device=q_chunk.device)
@@ -123,7 +152,7 @@ def prefill_paged(q_chunk, k_pool, v_pool, page_table, *, cache_len, block, out_
 
 
 def backward(q, k, v, out, lse, dout, *, cache_len=0, causal=True, scale=None, dq=None, dk=None, dv=None,
-             accumulate=False, grad_dtype=torch.float32):
+             accumulate=False, grad_dtype=torch.float32, workspace=None):
     """dQ, dK, dV of Out for (chunked) prefill.
 
     q, dout [B,C,Hq,128] bf16; k, v [B,S_max,Hkv,128] bf16 (keys [0, cache_len+C)
@@ -131,9 +160,13 @@ def backward(q, k, v, out, lse, dout, *, cache_len=0, causal=True, scale=None, d
     Returns (dq [B,C,Hq,128], dk, dv [B,S_max,Hkv,128]) in grad_dtype (fp32, or
     bf16 rounded once from the fp32 result); dk/dv rows past cache_len+C are left
     as given (zeros when allocated here).  With ``accumulate`` (fp32 only) the
-    call adds to the given dk/dv."""
-    B, C, Hq, D = q.shape
-    S_max, Hkv = k.shape[1], k.shape[2]
+    call adds to the given dk/dv.  The per-row scratch is ``workspace`` (allocated
+    here unless given)."""
+    B, C, Hq, Hkv, S_max = _checks.backward(q.shape, k.shape, v.shape, out.shape, lse.shape, dout.shape,
+                                            int(cache_len), None if dq is None else dq.shape,
+                                            None if dk is None else dk.shape, None if dv is None else dv.shape)
+    _same_device(q, k, v, out, lse, dout, dq, dk, dv, workspace)
+    D = q.shape[3]
     if out.dtype not in _OUT_DT:
         raise ValueError(f"out must be bf16 or fp32, got {out.dtype}")
     p = params(Hq, Hkv, block=128, out_dtype=out.dtype, causal=causal, scale=scale, head_dim=D)
@@ -145,32 +178,35 @@ def backward(q, k, v, out, lse, dout, *, cache_len=0, causal=True, scale=None, d
     if dv is None:
         dv = torch.zeros((B, S_max, Hkv, D), dtype=grad_dtype, device=q.device)
     lib = _lib.load()
+    ws, ws_bytes = _ws(workspace, int(lib.rla_backward_workspace_bytes(ctypes.byref(p), B, C)), q.device)
     _lib.check(lib.rla_attn_backward(
         ctypes.byref(p), _dev(q, "q", torch.bfloat16, 4), _dev(k, "k", torch.bfloat16, 4),
         _dev(v, "v", torch.bfloat16, 4), _dev(out, "out", out.dtype, 4), _dev(lse, "lse", torch.float32, 3),
         _dev(dout, "dout", torch.bfloat16, 4), B, C, int(cache_len), S_max, int(bool(accumulate)),
         _OUT_DT[grad_dtype], _dev(dq, "dq", grad_dtype, 4), _dev(dk, "dk", grad_dtype, 4),
-        _dev(dv, "dv", grad_dtype, 4), _stream(q.device)))
+        _dev(dv, "dv", grad_dtype, 4), ws.data_ptr(), ws_bytes, _stream(q.device)))
     return dq, dk, dv
 
 
-def lm_head_logprobs(x, w, tokens):
+def lm_head_logprobs(x, w, tokens, *, workspace=None):
     """Selected log-probabilities through an FP32 lm_head.  x [T, H] (or any
     [T, ...] contiguous tensor, flattened per token) bf16 or fp32; w [V, H]
-    fp32; tokens [T] int32.  Returns (logp [T], logz [T]) fp32."""
+    fp32; tokens [T] int32.  Returns (logp [T], logz [T]) fp32.  Scratch comes
+    from ``workspace`` (allocated here unless given)."""
     T = x.shape[0]
     xf = x.reshape(T, -1)
-    V, H = w.shape
-    if xf.shape[1] != H:
-        raise ValueError(f"x has {xf.shape[1]} values per token, w has {H}")
+    T, H, V = _checks.lm_head(T, xf.shape[1], w.shape, tokens.shape)
+    _same_device(x, w, tokens, workspace)
     if x.dtype not in _OUT_DT:
         raise ValueError(f"x must be bf16 or fp32, got {x.dtype}")
     logp = torch.empty(T, dtype=torch.float32, device=x.device)
     logz = torch.empty(T, dtype=torch.float32, device=x.device)
     lib = _lib.load()
+    ws, ws_bytes = _ws(workspace, int(lib.rla_lm_head_workspace_bytes(T, V)), x.device)
     _lib.check(lib.rla_lm_head_logprobs(
         _dev(xf, "x", x.dtype, 2), _OUT_DT[x.dtype], _dev(w, "w", torch.float32, 2),
-        _dev(tokens, "tokens", torch.int32, 1), T, H, V, logp.data_ptr(), logz.data_ptr(), _stream(x.device)))
+        _dev(tokens, "tokens", torch.int32, 1), T, H, V, logp.data_ptr(), logz.data_ptr(), ws.data_ptr(), ws_bytes,
+        _stream(x.device)))
     return logp, logz
 
 
@@ -180,8 +216,12 @@ def emit_partials(q, k, v, kv_blocks, *, block, out_dtype=torch.bfloat16, causal
 
     Full prefill (cache_len None) or chunked (q is the chunk, k/v the caches).
     Returns (part_out [n,B*q_count,Hq,128] fp32, part_lse [n,B*q_count,Hq])."""
-    B, S, Hq, D = q.shape
-    Hkv = k.shape[2]
+    if cache_len is None:
+        B, S, Hq, Hkv = _checks.prefill(q.shape, k.shape, v.shape)
+    else:
+        B, S, Hq, Hkv, _ = _checks.chunked(q.shape, k.shape, v.shape, int(cache_len))
+    _same_device(q, k, v, part_out, part_lse)
+    D = q.shape[3]
     q_count = S - q_begin if q_count is None else q_count
     n = len(kv_blocks)
     rows = B * q_count
@@ -191,8 +231,7 @@ def emit_partials(q, k, v, kv_blocks, *, block, out_dtype=torch.bfloat16, causal
         part_lse = torch.empty((n, rows, Hq), dtype=torch.float32, device=q.device)
     _dev(part_out, "part_out", torch.float32)
     _dev(part_lse, "part_lse", torch.float32)
-    if part_out.numel() < n * rows * Hq * D or part_lse.numel() < n * rows * Hq:
-        raise ValueError("partial buffers too small")
+    _checks.partials(part_out.shape, part_lse.shape, n, rows, Hq)
     p = params(Hq, Hkv, block=block, out_dtype=out_dtype, causal=causal, scale=scale, head_dim=D)
     shard, keep = _shard_struct(kv_blocks, q_begin, q_count, part_out, part_lse, rows)
     lib = _lib.load()
@@ -202,7 +241,7 @@ def emit_partials(q, k, v, kv_blocks, *, block, out_dtype=torch.bfloat16, causal
                                   _stream(q.device))
     else:
         st = lib.rla_attn_prefill_chunked(ctypes.byref(p), qp, kp, vp, B, S, int(cache_len), k.shape[1],
-                                          ctypes.byref(shard), None, None, _stream(q.device))
+                                          ctypes.byref(shard), None, 0, None, None, _stream(q.device))
     del keep
     _lib.check(st)
     return part_out, part_lse
@@ -215,6 +254,8 @@ def merge_states(part_out, part_lse, global_block_index, *, Hq=None, out_dtype=t
     n, rows, Hq_, D = part_out.shape
     Hq = Hq_ if Hq is None else Hq
     n = n if n_parts is None else n_parts
+    _checks.partials(part_out.shape, part_lse.shape, n, rows, Hq)
+    _same_device(part_out, part_lse)
     p = params(Hq, Hq, block=128, out_dtype=out_dtype, head_dim=D, merge_order=order)
     arr, m = _i64_array(global_block_index)
     if m != n:
@@ -239,13 +280,15 @@ def decode_paged(q, k_pool, v_pool, page_table, ctx_lens, *, block, max_context_
     """Paged-KV decode.  q [Bd,Hq,128] bf16; pools [num_pages,Hkv,P,128] bf16;
     page_table [Bd,max_pages] int32; ctx_lens [Bd] int32 (device) ->
     (out [Bd,Hq,128], lse [Bd,Hq])."""
-    Bd, Hq, D = q.shape
-    num_pages, Hkv, P, _ = k_pool.shape
+    Bd, Hq, Hkv, num_pages, P, _ = _checks.decode(q.shape, k_pool.shape, v_pool.shape, page_table.shape,
+                                                  ctx_lens.shape, host_ctx_lens)
+    _same_device(q, k_pool, v_pool, page_table, ctx_lens, workspace)
+    D = q.shape[2]
     p = params(Hq, Hkv, block=block, out_dtype=out_dtype, scale=scale, head_dim=D)
     lib = _lib.load()
     need = int(lib.rla_decode_workspace_bytes(ctypes.byref(p), Bd, int(max_context_len)))
     if workspace is None:
-        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=q.device)
+        workspace = alloc_workspace(need, q.device)
     host = None
     if host_ctx_lens is not None:
         host = (ctypes.c_int32 * Bd)(*[int(x) for x in host_ctx_lens])

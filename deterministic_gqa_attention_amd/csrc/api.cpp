@@ -8,7 +8,6 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
-#include <mutex>
 #include <vector>
 
 #include "kernels.hpp"
@@ -17,8 +16,6 @@
 namespace {
 
 thread_local char g_err[512] = "";
-
-constexpr int kMaxDevices = 64;
 
 rla_status fail(rla_status st, const char* fmt, ...) {
   va_list ap;
@@ -228,64 +225,21 @@ rla_status run_decode(const rla_attn_params* p, int g, const void* q, const void
   return hip_status(e, "decode fold launch");
 }
 
-// Device scratch for one call, stream-ordered, from a memory pool of the
-// library's own that keeps what is freed (release threshold: unlimited), so
-// calls after the first reuse the pool's memory instead of allocating.
-hipError_t scratch_alloc(void** ptr, size_t bytes, hipStream_t s) {
-  static std::mutex mu;
-  static hipMemPool_t pools[kMaxDevices] = {};
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
-  {
-    std::lock_guard<std::mutex> lock(mu);
-    if (pools[dev] == nullptr) {
-      hipMemPoolProps props;
-      std::memset(&props, 0, sizeof props);
-      props.allocType = hipMemAllocationTypePinned;
-      props.location.type = hipMemLocationTypeDevice;
-      props.location.id = dev;
-      hipMemPool_t pool = nullptr;
-      e = hipMemPoolCreate(&pool, &props);
-      if (e != hipSuccess) return e;
-      uint64_t keep = UINT64_MAX;
-      e = hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep);
-      if (e != hipSuccess) return e;
-      pools[dev] = pool;
-    }
-  }
-  return hipMallocFromPoolAsync(ptr, bytes, pools[dev], s);
-}
-
 // A chunk of one query is a decode step over the cache: the contiguous cache
 // [B][s_max][Hkv][128] is a paged pool with one key per page (page id
 // b*s_max + j), so the decode kernels run it, spreading the KV blocks over
 // many workgroups and folding the block items in order.  Their per-(row,
 // block) arithmetic is that of the prefill kernels, so the bits are the same.
-// Returns false (nothing done) when the cache is too large for int32 page ids.
-bool single_query_chunk(const rla_attn_params* p, int g, const void* q, const void* k_cache, const void* v_cache,
-                        int32_t batch, int32_t cache_len, int32_t s_max, void* out, float* lse, hipStream_t s,
-                        rla_status* st) {
-  if (static_cast<int64_t>(batch) * s_max > 0x7fffffff) return false;
-  const int32_t len = cache_len + 1;
-  const size_t bytes = rla_decode_workspace_bytes(p, batch, len);
-  void* ws = nullptr;
-  hipError_t e = scratch_alloc(&ws, bytes, s);
-  if (e != hipSuccess) {
-    *st = hip_status(e, "chunk scratch");
-    return true;
-  }
-  *st = run_decode(p, g, q, k_cache, v_cache, static_cast<int64_t>(batch) * s_max, 1, nullptr, s_max, nullptr, len,
-                   nullptr, batch, len, len, ws, out, lse, s);
-  e = hipFreeAsync(ws, s);
-  if (*st == RLA_OK && e != hipSuccess) *st = hip_status(e, "chunk scratch free");
-  return true;
+// The route is taken when the page ids fit int32 (no shard); its block items
+// go to the caller's workspace.
+bool single_query_route(int32_t batch, int32_t chunk_len, int32_t s_max, const rla_shard* shard) {
+  return chunk_len == 1 && shard == nullptr && static_cast<int64_t>(batch) * s_max <= 0x7fffffff;
 }
 
 }  // namespace
 
 extern "C" {
+
 
 const char* rla_last_error(void) { return g_err; }
 
@@ -299,24 +253,33 @@ rla_status rla_attn_prefill(const rla_attn_params* p, const void* q, const void*
   return prefill_common(p, q, k, v, batch, seq_len, 0, seq_len, seq_len, shard, out, lse, hip_stream);
 }
 
+size_t rla_chunked_workspace_bytes(const rla_attn_params* p, int32_t batch, int32_t chunk_len, int32_t cache_len,
+                                   int32_t s_max) {
+  if (batch < 1 || cache_len < 0 || s_max < 1 || !single_query_route(batch, chunk_len, s_max, nullptr)) return 0;
+  return rla_decode_workspace_bytes(p, batch, cache_len + 1);
+}
+
 rla_status rla_attn_prefill_chunked(const rla_attn_params* p, const void* q_chunk, const void* k_cache,
                                     const void* v_cache, int32_t batch, int32_t chunk_len, int32_t cache_len,
-                                    int32_t s_max, const rla_shard* shard, void* out, float* lse,
-                                    void* hip_stream) {
+                                    int32_t s_max, const rla_shard* shard, void* workspace,
+                                    size_t workspace_bytes, void* out, float* lse, void* hip_stream) {
   if (batch < 1 || chunk_len < 1 || cache_len < 0 || s_max < 1 ||
       static_cast<int64_t>(cache_len) + chunk_len > s_max)
     return fail(RLA_ERR_BAD_SHAPE, "need batch>=1, chunk_len>=1, cache_len>=0, cache_len+chunk_len<=s_max "
                 "(got %d, %d, %d, %d)", batch, chunk_len, cache_len, s_max);
-  if (chunk_len == 1 && shard == nullptr) {
+  if (single_query_route(batch, chunk_len, s_max, shard)) {
     int g = 0;
     const rla_status st0 = check_params(p, true, &g);
     if (st0 != RLA_OK) return st0;
-    if (q_chunk == nullptr || k_cache == nullptr || v_cache == nullptr || out == nullptr || lse == nullptr)
-      return fail(RLA_ERR_NULL_POINTER, "a required pointer is NULL");
-    rla_status st = RLA_OK;
-    if (single_query_chunk(p, g, q_chunk, k_cache, v_cache, batch, cache_len, s_max, out, lse,
-                           static_cast<hipStream_t>(hip_stream), &st))
-      return st;
+    if (q_chunk == nullptr || k_cache == nullptr || v_cache == nullptr || out == nullptr || lse == nullptr ||
+        workspace == nullptr)
+      return fail(RLA_ERR_NULL_POINTER, "a required pointer is NULL (a chunk of one query needs the workspace)");
+    const int32_t len = cache_len + 1;
+    const size_t need = rla_decode_workspace_bytes(p, batch, len);
+    if (workspace_bytes < need)
+      return fail(RLA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", workspace_bytes, need);
+    return run_decode(p, g, q_chunk, k_cache, v_cache, static_cast<int64_t>(batch) * s_max, 1, nullptr, s_max,
+                      nullptr, len, nullptr, batch, len, len, workspace, out, lse, static_cast<hipStream_t>(hip_stream));
   }
   return prefill_common(p, q_chunk, k_cache, v_cache, batch, chunk_len, cache_len,
                         static_cast<int64_t>(cache_len) + chunk_len, s_max, shard, out, lse, hip_stream);
@@ -422,12 +385,13 @@ rla_status rla_attn_decode_paged(const rla_attn_params* p, const void* q, const 
 rla_status rla_attn_backward(const rla_attn_params* p, const void* q, const void* k, const void* v,
                              const void* out, const float* lse, const void* dout, int32_t batch,
                              int32_t q_rows, int32_t cache_len, int32_t s_max, int32_t accumulate,
-                             rla_dtype grad_dtype, void* dq, void* dk, void* dv, void* hip_stream) {
+                             rla_dtype grad_dtype, void* dq, void* dk, void* dv, void* workspace,
+                             size_t workspace_bytes, void* hip_stream) {
   int g = 0;
   rla_status st = check_params(p, true, &g);
   if (st != RLA_OK) return st;
   if (q == nullptr || k == nullptr || v == nullptr || out == nullptr || lse == nullptr || dout == nullptr ||
-      dq == nullptr || dk == nullptr || dv == nullptr)
+      dq == nullptr || dk == nullptr || dv == nullptr || workspace == nullptr)
     return fail(RLA_ERR_NULL_POINTER, "a required pointer is NULL");
   if (batch < 1 || q_rows < 1 || cache_len < 0 || s_max < 1 || static_cast<int64_t>(cache_len) + q_rows > s_max)
     return fail(RLA_ERR_BAD_SHAPE, "need batch>=1, q_rows>=1, cache_len>=0, cache_len+q_rows<=s_max "
@@ -445,6 +409,9 @@ rla_status rla_attn_backward(const rla_attn_params* p, const void* q, const void
   if (!fits_32bit_offsets(kv_len, Hkv) || !fits_32bit_offsets(sq_pad, Hq) || sq_pad > 0x7fffffff)
     return fail(RLA_ERR_UNSUPPORTED, "sequence too long: one head's rows must span < 2 GiB (q_rows=%d, kv_len=%lld)",
                 q_rows, (long long)kv_len);
+  const size_t need = rla_backward_workspace_bytes(p, batch, q_rows);
+  if (workspace_bytes < need)
+    return fail(RLA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", workspace_bytes, need);
 
   rla::BackwardArgs a;
   std::memset(&a, 0, sizeof a);
@@ -477,25 +444,33 @@ rla_status rla_attn_backward(const rla_attn_params* p, const void* q, const void
   a.c = score_scale(p);
   a.scale = p->softmax_scale;
 
-  hipStream_t s = static_cast<hipStream_t>(hip_stream);
-  const size_t ws_bytes = static_cast<size_t>(batch) * Hq * 2 * static_cast<size_t>(sq_pad) * sizeof(float);
-  void* ws = nullptr;
-  hipError_t e = scratch_alloc(&ws, ws_bytes, s);
-  if (e != hipSuccess) return hip_status(e, "backward scratch");
-  a.ws = static_cast<float*>(ws);
-  e = rla::launch_backward(a, p->out_dtype == RLA_DT_FP32, s);
-  const hipError_t ef = hipFreeAsync(ws, s);
-  if (e != hipSuccess) return hip_status(e, "backward launch");
-  return hip_status(ef, "backward scratch free");
+  a.ws = static_cast<float*>(workspace);
+  return hip_status(rla::launch_backward(a, p->out_dtype == RLA_DT_FP32, static_cast<hipStream_t>(hip_stream)),
+                    "backward launch");
+}
+
+size_t rla_backward_workspace_bytes(const rla_attn_params* p, int32_t batch, int32_t q_rows) {
+  if (check_params(p, true, nullptr) != RLA_OK || batch < 1 || q_rows < 1) return 0;
+  const size_t sq_pad = (static_cast<size_t>(q_rows) + 63) / 64 * 64;
+  return static_cast<size_t>(batch) * p->num_q_heads * 2 * sq_pad * sizeof(float);
+}
+
+size_t rla_lm_head_workspace_bytes(int32_t T, int32_t V) {
+  if (T < 1 || V < 1) return 0;
+  return rla::lm_head_scratch_floats(T, V) * sizeof(float);
 }
 
 rla_status rla_lm_head_logprobs(const void* x, rla_dtype x_dtype, const float* w, const int32_t* tokens, int32_t T,
-                                int32_t H, int32_t V, float* logp, float* logz, void* hip_stream) {
-  if (x == nullptr || w == nullptr || tokens == nullptr || logp == nullptr)
+                                int32_t H, int32_t V, float* logp, float* logz, void* workspace,
+                                size_t workspace_bytes, void* hip_stream) {
+  if (x == nullptr || w == nullptr || tokens == nullptr || logp == nullptr || workspace == nullptr)
     return fail(RLA_ERR_NULL_POINTER, "a required pointer is NULL");
   if (x_dtype != RLA_DT_BF16 && x_dtype != RLA_DT_FP32) return fail(RLA_ERR_UNSUPPORTED, "x_dtype=%d unsupported", x_dtype);
   if (T < 1 || H < 8 || H % 8 != 0 || V < 1)
     return fail(RLA_ERR_BAD_SHAPE, "need T>=1, H>=8 with H %% 8 == 0, V>=1 (got %d, %d, %d)", T, H, V);
+  const size_t need = rla_lm_head_workspace_bytes(T, V);
+  if (workspace_bytes < need)
+    return fail(RLA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", workspace_bytes, need);
   rla::LmHeadArgs a;
   std::memset(&a, 0, sizeof a);
   a.x = x;
@@ -506,16 +481,9 @@ rla_status rla_lm_head_logprobs(const void* x, rla_dtype x_dtype, const float* w
   a.T = T;
   a.H = H;
   a.V = V;
-  hipStream_t s = static_cast<hipStream_t>(hip_stream);
-  const size_t bytes = rla::lm_head_scratch_floats(T, V) * sizeof(float);
-  void* ws = nullptr;
-  hipError_t e = scratch_alloc(&ws, bytes, s);
-  if (e != hipSuccess) return hip_status(e, "lm_head scratch");
-  a.part = static_cast<float*>(ws);  // the launcher places zsel after the block partials
-  e = rla::launch_lm_head(a, x_dtype == RLA_DT_FP32, s);
-  const hipError_t ef = hipFreeAsync(ws, s);
-  if (e != hipSuccess) return hip_status(e, "lm_head launch");
-  return hip_status(ef, "lm_head scratch free");
+  a.part = static_cast<float*>(workspace);  // the launcher places zsel after the block partials
+  return hip_status(rla::launch_lm_head(a, x_dtype == RLA_DT_FP32, static_cast<hipStream_t>(hip_stream)),
+                    "lm_head launch");
 }
 
 rla_status rla_merge_states(const rla_attn_params* p, const rla_partials* parts, void* out, float* lse,

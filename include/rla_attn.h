@@ -36,7 +36,10 @@
  *  - Work is enqueued on `hip_stream` (a hipStream_t, NULL = default stream)
  *    and is asynchronous; device faults surface at the caller's synchronize.
  *    A launch failure returns RLA_ERR_HIP.
- *  - No call allocates device memory; scratch space is caller-provided.
+ *  - No call allocates device memory: scratch space is caller-provided device
+ *    memory whose size the matching rla_*_workspace_bytes query returns; a
+ *    workspace smaller than that is rejected with RLA_ERR_WORKSPACE_TOO_SMALL
+ *    before anything is enqueued.
  *  - Thread safety: stateless apart from the thread-local error string.
  *  - Empty rows (no visible key) give Out = 0 and LSE = -inf.
  */
@@ -114,7 +117,11 @@ typedef struct {
                                          lse [n_kv_blocks][batch*q_count][Hq]  */
 } rla_shard;
 
-/* Full (causal) prefill over `batch` sequences of `seq_len` tokens.
+/* Full (causal) prefill over `batch` sequences of `seq_len` tokens ("WS2
+ * Attention PR5 Drift Benchmark", section "Scope": full prefill of the
+ * Qwen3-8B attention shape on post-RoPE Q/K, CP=1 or CP=2; "Transformer
+ * Engine Reuse": one partial state per KV block, merged in global block index
+ * order).
  * q [batch][seq_len][Hq][128], k, v [batch][seq_len][Hkv][128] bf16, post-RoPE.
  * shard == NULL: fused path, writes out [batch][seq_len][Hq][128] (bf16 or fp32
  * per out_dtype) and lse [batch][seq_len][Hq].  shard != NULL: emit path, writes
@@ -133,13 +140,21 @@ rla_status rla_attn_prefill(const rla_attn_params* p, const void* q, const void*
  * shard as in rla_attn_prefill (q_begin/q_count relative to the chunk).
  * A chunk of one query without a shard runs as a decode step (the cache read
  * as a pool of one-key pages: KV blocks spread over many workgroups, block
- * items folded in order); it takes its item scratch, stream-ordered, from a
- * device memory pool the library keeps (allocated on first use, reused
- * after).  The result bits do not depend on the route. */
+ * items folded in order); its block items go to `workspace`, which must hold
+ * rla_chunked_workspace_bytes(p, batch, chunk_len, cache_len, s_max) bytes of
+ * device memory (RLA_ERR_WORKSPACE_TOO_SMALL otherwise; contents on return
+ * unspecified).  Every other call needs no workspace (it may be NULL, size 0).
+ * The result bits do not depend on the route. */
 rla_status rla_attn_prefill_chunked(const rla_attn_params* p, const void* q_chunk, const void* k_cache,
                                     const void* v_cache, int32_t batch, int32_t chunk_len,
-                                    int32_t cache_len, int32_t s_max, const rla_shard* shard, void* out,
-                                    float* lse, void* hip_stream);
+                                    int32_t cache_len, int32_t s_max, const rla_shard* shard, void* workspace,
+                                    size_t workspace_bytes, void* out, float* lse, void* hip_stream);
+
+/* Workspace bytes rla_attn_prefill_chunked needs without a shard: the decode
+ * workspace of `batch` sequences of cache_len + 1 keys for a chunk of one
+ * query, else 0 (also 0 on invalid arguments). */
+size_t rla_chunked_workspace_bytes(const rla_attn_params* p, int32_t batch, int32_t chunk_len, int32_t cache_len,
+                                   int32_t s_max);
 
 /* Paged chunked prefill ("Commands": paged prefill/decode with batch and
  * page-layout invariance): rla_attn_prefill_chunked with the keys gathered
@@ -169,11 +184,13 @@ rla_status rla_attn_prefill_paged(const rla_attn_params* p, const void* q_chunk,
  * page_table[s][j / page_size] in the pools.
  * q [batch][Hq][128]; k_pool, v_pool [num_pages][Hkv][page_size][128] bf16;
  * page_table [batch][max_pages_per_seq] int32 (device); context_lens [batch]
- * int32 (device).  The kernels read the lengths from context_lens;
- * host_context_lens [host][batch] may be NULL.  When given, the lengths are
+ * int32 (device).  host_context_lens [host][batch] may be NULL; when given it
+ * must hold the same lengths as context_lens (the launch is sized from the host
+ * copy and the kernels read the device copy, so a device length above its host
+ * length leaves blocks uncomputed: unspecified result).  The host lengths are
  * validated against max_context_len and the table width before anything is
- * enqueued and the launch covers exactly the blocks they need; without it the
- * launch covers every block up to max_context_len and idle workgroups exit
+ * enqueued and the launch covers exactly the blocks they need; without them
+ * the launch covers every block up to max_context_len and idle workgroups exit
  * (the results are the same bits either way).  page_size must divide
  * kv_block_size.  Lengths above
  * min(max_context_len, max_pages_per_seq*page_size) are clamped to it, and a
@@ -221,13 +238,18 @@ rla_status rla_merge_states(const rla_attn_params* p, const rla_partials* parts,
  * of 64 rows in ascending order, q heads of the group in ascending order
  * inside a tile; dQ: keys in ascending order), so results do not depend on
  * the batch makeup or on scheduling.  P and dS are rounded to bf16 as MFMA
- * operands; dS includes softmax_scale.  kv_block_size is not used.  Takes a
- * per-row scratch (8 bytes per query row and head), stream-ordered, from the
- * library's device memory pool. */
+ * operands; dS includes softmax_scale.  kv_block_size is not used.
+ * workspace: at least rla_backward_workspace_bytes(p, batch, q_rows) bytes of
+ * device memory (per-row LSE and Delta, 8 bytes per query row and head, rows
+ * padded to 64); contents on return unspecified. */
 rla_status rla_attn_backward(const rla_attn_params* p, const void* q, const void* k, const void* v,
                              const void* out, const float* lse, const void* dout, int32_t batch,
                              int32_t q_rows, int32_t cache_len, int32_t s_max, int32_t accumulate,
-                             rla_dtype grad_dtype, void* dq, void* dk, void* dv, void* hip_stream);
+                             rla_dtype grad_dtype, void* dq, void* dk, void* dv, void* workspace,
+                             size_t workspace_bytes, void* hip_stream);
+
+/* Workspace bytes rla_attn_backward needs (0 on invalid arguments). */
+size_t rla_backward_workspace_bytes(const rla_attn_params* p, int32_t batch, int32_t q_rows);
 
 /* Selected log-probability through an FP32 lm_head ("WS2 Attention PR5 Drift
  * Benchmark", section "Scope": both attention outputs of a drift comparison go
@@ -241,11 +263,17 @@ rla_status rla_attn_backward(const rla_attn_params* p, const void* q, const void
  * tensor [T][Hq][128] read as H = Hq*128; w [V][H] fp32 device; tokens [T]
  * int32 device; logp [T] fp32 device; logz [T] fp32 device or NULL.  H must be
  * a positive multiple of 8.  A token id outside [0, V) gives logp = NaN.
- * A token's results do not depend on the other tokens of the call.  Takes
- * (ceil(V/32) * T * 2 + T) floats of scratch, stream-ordered, from the
- * library's device memory pool. */
+ * A token's results do not depend on the other tokens of the call.
+ * workspace: at least rla_lm_head_workspace_bytes(T, V) bytes of device memory
+ * (per-block partial sums and the selected logits); contents on return
+ * unspecified. */
 rla_status rla_lm_head_logprobs(const void* x, rla_dtype x_dtype, const float* w, const int32_t* tokens,
-                                int32_t T, int32_t H, int32_t V, float* logp, float* logz, void* hip_stream);
+                                int32_t T, int32_t H, int32_t V, float* logp, float* logz, void* workspace,
+                                size_t workspace_bytes, void* hip_stream);
+
+/* Workspace bytes rla_lm_head_logprobs needs: (ceil(V/32) * T * 2 + T) floats
+ * (0 on invalid arguments). */
+size_t rla_lm_head_workspace_bytes(int32_t T, int32_t V);
 
 /* Workspace bytes rla_attn_decode_paged needs (0 on invalid arguments). */
 size_t rla_decode_workspace_bytes(const rla_attn_params* p, int32_t batch, int32_t max_context_len);

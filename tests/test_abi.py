@@ -78,11 +78,26 @@ def test_prefill_rejects_null_and_shapes(lib):
 
 def test_chunked_rejects_overflowing_cache(lib):
     p = _params()
-    st = lib.rla_attn_prefill_chunked(ctypes.byref(p), FAKE, FAKE, FAKE, 1, 64, 4000, 4032, None, FAKE, FAKE,
-                                      None)
+    st = lib.rla_attn_prefill_chunked(ctypes.byref(p), FAKE, FAKE, FAKE, 1, 64, 4000, 4032, None, None, 0, FAKE,
+                                      FAKE, None)
     assert st == 2 and "s_max" in lib.rla_last_error().decode()
-    st = lib.rla_attn_prefill_chunked(ctypes.byref(p), FAKE, FAKE, FAKE, 1, 0, 0, 4032, None, FAKE, FAKE, None)
+    st = lib.rla_attn_prefill_chunked(ctypes.byref(p), FAKE, FAKE, FAKE, 1, 0, 0, 4032, None, None, 0, FAKE, FAKE,
+                                      None)
     assert st == 2
+
+
+def test_chunk_of_one_needs_its_workspace(lib):
+    """A single-query chunk runs as a decode step over the cache and takes its
+    block items from the caller's workspace; nothing is allocated inside."""
+    p = _params()
+    need = lib.rla_chunked_workspace_bytes(ctypes.byref(p), 2, 1, 4095, 8192)
+    assert need == lib.rla_decode_workspace_bytes(ctypes.byref(p), 2, 4096) > 0
+    assert lib.rla_chunked_workspace_bytes(ctypes.byref(p), 2, 64, 4032, 8192) == 0   # prefill route
+    assert lib.rla_chunked_workspace_bytes(ctypes.byref(_params(head_dim=64)), 2, 1, 4095, 8192) == 0
+    call = lambda ws, nbytes: lib.rla_attn_prefill_chunked(ctypes.byref(p), FAKE, FAKE, FAKE, 2, 1, 4095, 8192, None,
+                                                           ws, nbytes, FAKE, FAKE, None)
+    assert call(None, need) == 1
+    assert call(FAKE, need - 1) == 5 and "workspace" in lib.rla_last_error().decode()
 
 
 def test_prefill_rejects_rows_beyond_32bit_offsets(lib):
@@ -91,7 +106,7 @@ def test_prefill_rejects_rows_beyond_32bit_offsets(lib):
     st = lib.rla_attn_prefill(ctypes.byref(p), FAKE, FAKE, FAKE, 1, (1 << 18) + 1, None, FAKE, FAKE, None)
     assert st == 3 and "2 GiB" in lib.rla_last_error().decode()
     st = lib.rla_attn_prefill_chunked(ctypes.byref(p), FAKE, FAKE, FAKE, 1, 16, (1 << 20), (1 << 20) + 16, None,
-                                      FAKE, FAKE, None)  # Hkv=8: 2^20 keys span 2 GiB
+                                      None, 0, FAKE, FAKE, None)  # Hkv=8: 2^20 keys span 2 GiB
     assert st == 3 and "2 GiB" in lib.rla_last_error().decode()
 
 
@@ -171,9 +186,15 @@ def test_decode_validation_and_workspace(lib):
 def test_backward_rejects_bad_args(lib):
     """The backward entry validates pointers, shapes, the accumulate flag and
     the parameter contract before anything is enqueued."""
-    call = lambda p, b, rows, cache, smax, acc=0, q=FAKE, dq=FAKE, gdt=_lib.RLA_DT_FP32: lib.rla_attn_backward(
-        ctypes.byref(p), q, FAKE, FAKE, FAKE, FAKE, FAKE, b, rows, cache, smax, acc, gdt, dq, FAKE, FAKE, None)
+    call = lambda p, b, rows, cache, smax, acc=0, q=FAKE, dq=FAKE, gdt=_lib.RLA_DT_FP32, ws=FAKE, wsb=1 << 40: \
+        lib.rla_attn_backward(ctypes.byref(p), q, FAKE, FAKE, FAKE, FAKE, FAKE, b, rows, cache, smax, acc, gdt, dq,
+                              FAKE, FAKE, ws, wsb, None)
     p = _params()
+    need = lib.rla_backward_workspace_bytes(ctypes.byref(p), 2, 100)
+    assert need == 2 * 32 * 2 * 128 * 4                     # 8 bytes per row and head, rows padded to 64
+    assert lib.rla_backward_workspace_bytes(ctypes.byref(p), 2, 0) == 0
+    assert call(p, 2, 100, 0, 100, ws=None) == 1
+    assert call(p, 2, 100, 0, 100, wsb=need - 1) == 5
     assert call(p, 1, 16, 0, 16, q=None) == 1
     assert call(p, 1, 16, 0, 16, dq=None) == 1
     assert call(p, 0, 16, 0, 16) == 2
@@ -192,8 +213,13 @@ def test_backward_rejects_bad_args(lib):
 
 def test_lm_head_rejects_bad_args(lib):
     """Pointers, dtype and shapes are checked before anything is enqueued."""
-    call = lambda x, dt, T, H, V, w=FAKE, lp=FAKE: lib.rla_lm_head_logprobs(x, dt, w, FAKE, T, H, V, lp, None,
-                                                                           None)
+    call = lambda x, dt, T, H, V, w=FAKE, lp=FAKE, ws=FAKE, wsb=1 << 40: lib.rla_lm_head_logprobs(
+        x, dt, w, FAKE, T, H, V, lp, None, ws, wsb, None)
+    need = lib.rla_lm_head_workspace_bytes(64, 151936)
+    assert need == (-(-151936 // 32) * 64 * 2 + 64) * 4
+    assert lib.rla_lm_head_workspace_bytes(0, 10) == 0
+    assert call(FAKE, 0, 64, 4096, 151936, ws=None) == 1
+    assert call(FAKE, 0, 64, 4096, 151936, wsb=need - 1) == 5
     assert call(None, 0, 4, 64, 10) == 1
     assert call(FAKE, 0, 4, 64, 10, w=None) == 1
     assert call(FAKE, 0, 4, 64, 10, lp=None) == 1

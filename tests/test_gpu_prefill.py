@@ -1,7 +1,7 @@
 """GPU prefill parity against the FP64 oracle (through the C ABI).
 
-Small cases run every row; full-size cases (the long prefill workloads) check
-sampled rows, which the oracle computes one by one.
+Every case checks every row of Out and LSE except the S=32768 workload, which
+checks rows stratified over every 32-row tile plus the first and last blocks.
 """
 import numpy as np
 import pytest
@@ -10,7 +10,7 @@ import torch
 import oracle
 from deterministic_gqa_attention_amd import api
 from deterministic_gqa_attention_amd import inputs as gen
-from tests.gpu_util import assert_bitwise, check_parity, dev_bf16, host_f64, sample_rows, say
+from tests.gpu_util import assert_bitwise, check_parity, dev_bf16, host_f64, say
 
 pytestmark = pytest.mark.gpu
 
@@ -108,20 +108,32 @@ def test_repeat_run_bitwise():
 
 
 @pytest.mark.slow
-def test_full_prefill_b4_s4096_sampled():
-    """Full causal prefill B=4, S=4096, Hq=32, Hkv=8, 128-key blocks (the timed
-    workload), checked on sampled rows of every sequence."""
+def test_full_prefill_b4_s4096_all_rows():
+    """Full causal prefill B=4, S=4096, Hq=32, Hkv=8, 128-key blocks, bf16 Out
+    (the timed workload and launch): every row of Out and LSE against the
+    oracle."""
     cfg = gen.CFG2
     q, k, v = gen.prefill_inputs(cfg)
-    rows_t = sample_rows(cfg.S, 6, seed=2)
-    rows = np.concatenate([b * cfg.S + rows_t[(b * 7) % 3::2] for b in range(cfg.B)])
-    _run_and_check(q, k, v, block=cfg.block, out_dtype=torch.bfloat16, rows=rows, what="B=4 S=4096 sampled")
+    _run_and_check(q, k, v, block=cfg.block, out_dtype=torch.bfloat16, what="B=4 S=4096 all rows")
+
+
+def stratified_rows(S: int, tile: int = 32, block: int = 128) -> np.ndarray:
+    """Rows of a long sequence covering every tile of `tile` rows (two rows per
+    tile, so every offset within a tile occurs S / tile / 16 times), plus every
+    row of the first and the last KV block."""
+    t = np.arange(S // tile, dtype=np.int64)
+    rows = np.concatenate([t * tile + t % tile, t * tile + (t * 7 + 13) % tile,
+                           np.arange(block), np.arange(S - block, S)])
+    return np.unique(rows)
 
 
 @pytest.mark.slow
-def test_long_context_s32768_sampled():
-    """S=32768, Q/K scaled by 4, 128-key blocks: sampled rows, bf16 Out + LSE."""
+def test_long_context_s32768_stratified():
+    """S=32768, Q/K scaled by 4, 128-key blocks, bf16 Out + LSE: 2048 rows that
+    cover every 32-row tile and every offset within a tile, plus the first and
+    last 128-key blocks in full, against the oracle."""
     cfg = gen.CFG5
     q, k, v = gen.prefill_inputs(cfg)
-    rows = sample_rows(cfg.S, 4, seed=5)
-    _run_and_check(q, k, v, block=cfg.block, out_dtype=torch.bfloat16, rows=rows, what="S=32768 x4 sampled")
+    rows = stratified_rows(cfg.S)
+    assert len(rows) >= 2048
+    _run_and_check(q, k, v, block=cfg.block, out_dtype=torch.bfloat16, rows=rows, what="S=32768 x4 stratified")

@@ -22,7 +22,8 @@ RLA_MAX_PARTS = 512
 EXPORTS = ("rla_attn_prefill", "rla_attn_prefill_chunked", "rla_attn_prefill_paged", "rla_attn_decode_paged",
            "rla_merge_states", "rla_attn_backward", "rla_lm_head_logprobs", "rla_decode_workspace_bytes",
            "rla_chunked_workspace_bytes", "rla_backward_workspace_bytes", "rla_lm_head_workspace_bytes",
-           "rla_last_error", "rla_core_id")
+           "rla_attn_decode_paged_static", "rla_last_error", "rla_core_id")
+RLA_DECODE_STATIC_SCRATCH_BYTES = 132 << 20
 
 
 class RlaParams(ctypes.Structure):
@@ -75,6 +76,9 @@ def load(path: str = LIB_PATH):
     lib.rla_attn_decode_paged.argtypes = [pp, P, P, P, i64, i32, P, i32, P, ctypes.POINTER(ctypes.c_int32),
                                           i32, i32, P, sz, P, P, P]
     lib.rla_attn_decode_paged.restype = ctypes.c_int
+    lib.rla_attn_decode_paged_static.argtypes = [pp, P, P, P, i64, i32, P, i32, P, ctypes.POINTER(ctypes.c_int32),
+                                                 i32, i32, P, P, P]
+    lib.rla_attn_decode_paged_static.restype = ctypes.c_int
     lib.rla_attn_backward.argtypes = [pp, P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, P, P, P, P, sz, P]
     lib.rla_attn_backward.restype = ctypes.c_int
     lib.rla_lm_head_logprobs.argtypes = [P, i32, P, P, i32, i32, i32, P, P, P, sz, P]

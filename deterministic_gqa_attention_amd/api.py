@@ -17,7 +17,7 @@ from ._lib import RLAError, RlaParams, RlaPartials, RlaShard
 
 __all__ = ["RLAError", "core_id", "prefill", "prefill_chunked", "prefill_paged", "emit_partials",
            "merge_states", "decode_paged", "decode_workspace_bytes", "backward", "lm_head_logprobs", "params",
-           "alloc_workspace"]
+           "alloc_workspace", "decode_paged_static"]
 
 _OUT_DT = {torch.bfloat16: _lib.RLA_DT_BF16, torch.float32: _lib.RLA_DT_FP32}
 _ORDER = {"global_block_index": _lib.RLA_ORDER_GLOBAL_BLOCK_INDEX, "arrival": _lib.RLA_ORDER_ARRIVAL}
@@ -300,4 +300,29 @@ def decode_paged(q, k_pool, v_pool, page_table, ctx_lens, *, block, max_context_
         page_table.shape[1], _dev(ctx_lens, "ctx_lens", torch.int32, 1), host, Bd, int(max_context_len),
         _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(), out.data_ptr(),
         lse.data_ptr(), _stream(q.device)))
+    return out, lse
+
+
+def decode_paged_static(q, k_pool, v_pool, page_table, ctx_lens, *, block, max_context_len, host_ctx_lens=None,
+                        out_dtype=torch.bfloat16, scale=None):
+    """Paged-KV decode through rla_attn_decode_paged_static: the block items go
+    to the library's fixed device array instead of a workspace (no allocation
+    besides the outputs here; calls overlapping on one GPU race).  Same
+    arguments and bits as ``decode_paged``."""
+    Bd, Hq, Hkv, num_pages, P, _ = _checks.decode(q.shape, k_pool.shape, v_pool.shape, page_table.shape,
+                                                  ctx_lens.shape, host_ctx_lens)
+    _same_device(q, k_pool, v_pool, page_table, ctx_lens)
+    D = q.shape[2]
+    p = params(Hq, Hkv, block=block, out_dtype=out_dtype, scale=scale, head_dim=D)
+    lib = _lib.load()
+    host = None
+    if host_ctx_lens is not None:
+        host = (ctypes.c_int32 * Bd)(*[int(x) for x in host_ctx_lens])
+    out = torch.empty((Bd, Hq, D), dtype=out_dtype, device=q.device)
+    lse = torch.empty((Bd, Hq), dtype=torch.float32, device=q.device)
+    _lib.check(lib.rla_attn_decode_paged_static(
+        ctypes.byref(p), _dev(q, "q", torch.bfloat16, 3), _dev(k_pool, "k_pool", torch.bfloat16, 4),
+        _dev(v_pool, "v_pool", torch.bfloat16, 4), num_pages, P, _dev(page_table, "page_table", torch.int32, 2),
+        page_table.shape[1], _dev(ctx_lens, "ctx_lens", torch.int32, 1), host, Bd, int(max_context_len),
+        out.data_ptr(), lse.data_ptr(), _stream(q.device)))
     return out, lse

@@ -13,6 +13,9 @@
 #include "kernels.hpp"
 #include "rla_attn.h"
 
+static_assert(RLA_DECODE_STATIC_SCRATCH_BYTES == rla::kStaticDecodeScratchBytes,
+              "header and library disagree on the static decode scratch size");
+
 namespace {
 
 thread_local char g_err[512] = "";
@@ -236,6 +239,33 @@ bool single_query_route(int32_t batch, int32_t chunk_len, int32_t s_max, const r
   return chunk_len == 1 && shard == nullptr && static_cast<int64_t>(batch) * s_max <= 0x7fffffff;
 }
 
+// Validation shared by the two decode entry points (everything but the
+// workspace).  On success *group and *cap hold Hq/Hkv and the length cap.
+rla_status validate_decode(const rla_attn_params* p, const void* q, const void* k_pool, const void* v_pool,
+                           int64_t num_pages, int32_t page_size, const int32_t* page_table,
+                           int32_t max_pages_per_seq, const int32_t* context_lens, const int32_t* host_context_lens,
+                           int32_t batch, int32_t max_context_len, void* out, float* lse, int* group, int64_t* cap) {
+  rla_status st = check_params(p, true, group);
+  if (st != RLA_OK) return st;
+  if (q == nullptr || k_pool == nullptr || v_pool == nullptr || page_table == nullptr ||
+      context_lens == nullptr || out == nullptr || lse == nullptr)
+    return fail(RLA_ERR_NULL_POINTER, "a required pointer is NULL");
+  if (batch < 1 || max_context_len < 0 || num_pages < 1 || page_size < 1 || max_pages_per_seq < 1)
+    return fail(RLA_ERR_BAD_SHAPE, "need batch>=1, max_context_len>=0, num_pages>=1, page_size>=1, "
+                "max_pages_per_seq>=1");
+  if (p->kv_block_size % page_size != 0)
+    return fail(RLA_ERR_UNSUPPORTED, "page_size=%d must divide kv_block_size=%d", page_size, p->kv_block_size);
+  if (num_pages > 0x7fffffff) return fail(RLA_ERR_BAD_SHAPE, "num_pages exceeds int32 page ids");
+  *cap = std::min<int64_t>(max_context_len, static_cast<int64_t>(max_pages_per_seq) * page_size);
+  if (host_context_lens != nullptr) {
+    for (int i = 0; i < batch; ++i)
+      if (host_context_lens[i] < 0 || host_context_lens[i] > *cap)
+        return fail(RLA_ERR_BAD_SHAPE, "context_lens[%d]=%d outside [0, %lld]", i, host_context_lens[i],
+                    (long long)*cap);
+  }
+  return RLA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -356,29 +386,39 @@ rla_status rla_attn_decode_paged(const rla_attn_params* p, const void* q, const 
                                  void* workspace, size_t workspace_bytes, void* out, float* lse,
                                  void* hip_stream) {
   int g = 0;
-  rla_status st = check_params(p, true, &g);
+  int64_t cap = 0;
+  rla_status st = validate_decode(p, q, k_pool, v_pool, num_pages, page_size, page_table, max_pages_per_seq,
+                                  context_lens, host_context_lens, batch, max_context_len, out, lse, &g, &cap);
   if (st != RLA_OK) return st;
-  if (q == nullptr || k_pool == nullptr || v_pool == nullptr || page_table == nullptr ||
-      context_lens == nullptr || out == nullptr || lse == nullptr || workspace == nullptr)
-    return fail(RLA_ERR_NULL_POINTER, "a required pointer is NULL");
-  if (batch < 1 || max_context_len < 0 || num_pages < 1 || page_size < 1 || max_pages_per_seq < 1)
-    return fail(RLA_ERR_BAD_SHAPE, "need batch>=1, max_context_len>=0, num_pages>=1, page_size>=1, "
-                "max_pages_per_seq>=1");
-  if (p->kv_block_size % page_size != 0)
-    return fail(RLA_ERR_UNSUPPORTED, "page_size=%d must divide kv_block_size=%d", page_size, p->kv_block_size);
-  if (num_pages > 0x7fffffff) return fail(RLA_ERR_BAD_SHAPE, "num_pages exceeds int32 page ids");
-  const int64_t cap = std::min<int64_t>(max_context_len, static_cast<int64_t>(max_pages_per_seq) * page_size);
-  if (host_context_lens != nullptr) {
-    for (int i = 0; i < batch; ++i)
-      if (host_context_lens[i] < 0 || host_context_lens[i] > cap)
-        return fail(RLA_ERR_BAD_SHAPE, "context_lens[%d]=%d outside [0, %lld]", i, host_context_lens[i],
-                    (long long)cap);
-  }
+  if (workspace == nullptr) return fail(RLA_ERR_NULL_POINTER, "workspace is NULL");
   const size_t need = rla_decode_workspace_bytes(p, batch, max_context_len);
   if (workspace_bytes < need)
     return fail(RLA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", workspace_bytes, need);
   return run_decode(p, g, q, k_pool, v_pool, num_pages, page_size, page_table, max_pages_per_seq, context_lens, 0,
                     host_context_lens, batch, max_context_len, cap, workspace, out, lse,
+                    static_cast<hipStream_t>(hip_stream));
+}
+
+rla_status rla_attn_decode_paged_static(const rla_attn_params* p, const void* q, const void* k_pool,
+                                        const void* v_pool, int64_t num_pages, int32_t page_size,
+                                        const int32_t* page_table, int32_t max_pages_per_seq,
+                                        const int32_t* context_lens, const int32_t* host_context_lens,
+                                        int32_t batch, int32_t max_context_len, void* out, float* lse,
+                                        void* hip_stream) {
+  int g = 0;
+  int64_t cap = 0;
+  rla_status st = validate_decode(p, q, k_pool, v_pool, num_pages, page_size, page_table, max_pages_per_seq,
+                                  context_lens, host_context_lens, batch, max_context_len, out, lse, &g, &cap);
+  if (st != RLA_OK) return st;
+  const size_t need = rla_decode_workspace_bytes(p, batch, max_context_len);
+  if (need > RLA_DECODE_STATIC_SCRATCH_BYTES)
+    return fail(RLA_ERR_WORKSPACE_TOO_SMALL, "decode needs %zu bytes of block items, above the %zu-byte static "
+                "scratch of rla_attn_decode_paged_static", need, (size_t)RLA_DECODE_STATIC_SCRATCH_BYTES);
+  hipError_t e = hipSuccess;
+  void* scratch = rla::static_decode_scratch(&e);
+  if (scratch == nullptr) return hip_status(e, "static decode scratch");
+  return run_decode(p, g, q, k_pool, v_pool, num_pages, page_size, page_table, max_pages_per_seq, context_lens, 0,
+                    host_context_lens, batch, max_context_len, cap, scratch, out, lse,
                     static_cast<hipStream_t>(hip_stream));
 }
 

@@ -16,6 +16,8 @@
 // split over the four waves: wave w computes score sub-tile w and output dim
 // tile w, and the block max, sub-tile sums and bf16 P go through LDS.  Rows
 // are the group's q heads for the one query token (columns >= G are zero).
+#include <mutex>
+
 #include "kernels.hpp"
 #include "tile.hpp"
 
@@ -346,6 +348,38 @@ hipError_t launch_t(const DecodeArgs& a, hipStream_t s) {
 }
 
 }  // namespace
+
+// Block items of rla_attn_decode_paged_static (callers that cannot allocate):
+// a fixed device array, one copy per GPU the library runs on, held until the
+// process ends.  Host code never passes the array's name to a kernel (on the
+// host it only stands for the symbol); it uses the address
+// hipGetSymbolAddress gives for the current device.
+static __device__ __align__(256) char scratch[kStaticDecodeScratchBytes];
+
+void* static_decode_scratch(hipError_t* err) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* ptrs[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess && (dev < 0 || dev >= kMaxDevices)) e = hipErrorInvalidDevice;
+  if (e != hipSuccess) {
+    *err = e;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (ptrs[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr) {
+      *err = e != hipSuccess ? e : hipErrorInvalidSymbol;
+      return nullptr;
+    }
+    ptrs[dev] = ptr;
+  }
+  *err = hipSuccess;
+  return ptrs[dev];
+}
 
 hipError_t launch_decode_items(const DecodeArgs& a, int block, bool out_f32, hipStream_t s) {
   if (block == 128) return out_f32 ? launch_t<128, true>(a, s) : launch_t<128, false>(a, s);

@@ -140,6 +140,12 @@ hipError_t launch_backward(const BackwardArgs& a, bool out_f32, hipStream_t s);
 // Fused prefill with K/V gathered from paged pools (a.page_table etc. set).
 hipError_t launch_prefill_paged(const PrefillArgs& a, int block, bool out_f32, hipStream_t s);
 hipError_t launch_decode_items(const DecodeArgs& a, int block, bool out_f32, hipStream_t s);
+// Size of the fixed device array behind rla_attn_decode_paged_static: the
+// decode items of 64 sequences of 16384 keys with 32 q heads (129 MiB) fit.
+constexpr size_t kStaticDecodeScratchBytes = size_t{132} << 20;
+// Device address of that array on the current device (looked up once per
+// device); null with *err set on failure.
+void* static_decode_scratch(hipError_t* err);
 hipError_t launch_fold(const FoldArgs& a, bool decode, bool out_f32, hipStream_t s);
 
 }  // namespace rla

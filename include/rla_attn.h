@@ -206,6 +206,26 @@ rla_status rla_attn_decode_paged(const rla_attn_params* p, const void* q, const 
                                  int32_t batch, int32_t max_context_len, void* workspace,
                                  size_t workspace_bytes, void* out, float* lse, void* hip_stream);
 
+/* For callers that cannot allocate or provide device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation):
+ * rla_attn_decode_paged without the workspace argument.  The block items go
+ * to a fixed array inside the library, RLA_DECODE_STATIC_SCRATCH_BYTES of
+ * device memory per GPU the library runs on, held until the process ends; a
+ * call needing more (rla_decode_workspace_bytes above it) is rejected with
+ * RLA_ERR_WORKSPACE_TOO_SMALL before anything is enqueued.  The array is
+ * shared by every call on one GPU: calls that overlap in time on one GPU
+ * (different streams, different threads) race and give unspecified results;
+ * calls ordered on one stream are safe.  It allocates nothing (the array's
+ * device address is looked up once per device, on the first call there) and
+ * gives the same bits as rla_attn_decode_paged. */
+#define RLA_DECODE_STATIC_SCRATCH_BYTES ((size_t)132 << 20)
+rla_status rla_attn_decode_paged_static(const rla_attn_params* p, const void* q, const void* k_pool,
+                                        const void* v_pool, int64_t num_pages, int32_t page_size,
+                                        const int32_t* page_table, int32_t max_pages_per_seq,
+                                        const int32_t* context_lens, const int32_t* host_context_lens,
+                                        int32_t batch, int32_t max_context_len, void* out, float* lse,
+                                        void* hip_stream);
+
 /* Merge of partial states ("Transformer Engine Reuse"; "Scope":
  * merge_order_probe).  With RLA_ORDER_GLOBAL_BLOCK_INDEX the parts are folded
  * in ascending global_block_index whatever their arrival order; a repeated

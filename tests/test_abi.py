@@ -227,3 +227,21 @@ def test_lm_head_rejects_bad_args(lib):
     assert call(FAKE, 0, 0, 64, 10) == 2
     assert call(FAKE, 0, 4, 12, 10) == 2      # H not a multiple of 8
     assert call(FAKE, 0, 4, 64, 0) == 2
+
+
+def test_static_decode_rejects_oversize_before_touching_the_device(lib):
+    """rla_attn_decode_paged_static validates like rla_attn_decode_paged and
+    rejects a call whose block items exceed its fixed scratch before anything
+    reaches the device (this runs without a GPU)."""
+    p = _params()
+    cap = _lib.RLA_DECODE_STATIC_SCRATCH_BYTES
+    assert lib.rla_decode_workspace_bytes(ctypes.byref(p), 64, 16384) <= cap      # the paged-decode workload fits
+    assert lib.rla_decode_workspace_bytes(ctypes.byref(p), 70, 16384) > cap
+    host = (ctypes.c_int32 * 70)(*([100] * 70))
+    call = lambda b, mcl, ps=16, out=FAKE: lib.rla_attn_decode_paged_static(
+        ctypes.byref(p), FAKE, FAKE, FAKE, 1 << 16, ps, FAKE, 1024, FAKE, host, b, mcl, out, FAKE, None)
+    assert call(70, 16384) == 5 and "static scratch" in lib.rla_last_error().decode()
+    assert call(2, 16384, out=None) == 1
+    assert call(2, 16384, ps=48) == 3
+    host[0] = 20000
+    assert call(2, 16384) == 2

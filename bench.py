@@ -84,6 +84,51 @@ def kernel_source_hash() -> str:
     return h.hexdigest()
 
 
+def sha256_of(a) -> str:
+    """SHA-256 of a generated buffer's bytes (numpy stream stability across
+    versions is not guaranteed, so the record names exactly what was used)."""
+    return hashlib.sha256(np.ascontiguousarray(a).tobytes()).hexdigest()
+
+
+def git_commit():
+    """The commit of this tree when it is a git checkout (a copy without .git
+    gives None)."""
+    try:
+        import subprocess
+        r = subprocess.run(["git", "-C", ROOT, "rev-parse", "HEAD"], capture_output=True, text=True, timeout=10)
+        return r.stdout.strip() or None if r.returncode == 0 else None
+    except Exception:
+        return None
+
+
+def shard_manifest(cfg):
+    """The logical blocks of the emulated context-parallel shards of a prefill
+    workload: per logical CP rank, each owned global_block_index with its key
+    range, and the SHA-256 of that manifest (the block metadata hash of a
+    drift report)."""
+    ranks = []
+    for r, blocks in enumerate(cfg.shards):
+        ranks.append({"cp_rank": r, "blocks": [[int(b), int(b) * cfg.block, min(cfg.S, (int(b) + 1) * cfg.block)]
+                                               for b in blocks]})
+    text = json.dumps({"block": cfg.block, "S": cfg.S, "ranks": ranks}, sort_keys=True)
+    return {"kv_block_size": cfg.block, "n_blocks": cfg.n_blocks,
+            "ranks": [{"cp_rank": r["cp_rank"], "n_blocks": len(r["blocks"]),
+                       "key_ranges": _ranges([b[0] for b in r["blocks"]], cfg.block, cfg.S)} for r in ranks],
+            "sha256": hashlib.sha256(text.encode()).hexdigest()}
+
+
+def _ranges(blocks, block, S):
+    """Contiguous key ranges [lo, hi) covered by a sorted block list."""
+    out = []
+    for b in sorted(blocks):
+        lo, hi = b * block, min(S, (b + 1) * block)
+        if out and out[-1][1] == lo:
+            out[-1][1] = hi
+        else:
+            out.append([lo, hi])
+    return out
+
+
 def profile_traffic(path):
     """HBM bytes per launch recorded in a profile summary, if it was taken on
     the current kernel sources; else None."""
@@ -98,7 +143,8 @@ def profile_traffic(path):
 
 
 def cpu_baseline(q, k, v, cfg, seconds):
-    """Time the FP64 oracle on a seeded sample of query rows (all heads)."""
+    """Time the FP64 oracle on a seeded sample of query rows (all heads) of a
+    causal prefill workload."""
     import oracle
 
     rng = np.random.Generator(np.random.PCG64(1000 * cfg.cfg_id + 99))
@@ -122,7 +168,21 @@ def cpu_baseline(q, k, v, cfg, seconds):
                       f"({flops(rows):.3e} flop, {dt:.1f} s, FP64)"}
 
 
-def reported_legs(api, up, stream):
+def decode_cpu_baseline(d, dcfg):
+    """Time the FP64 oracle on the whole paged-decode workload (every sequence
+    and head; its 8.9e9 flop take seconds), as KV bytes scanned per second."""
+    import oracle
+    lens = d["ctx_lens"]
+    kv = gen.decode_kv_bytes(lens, dcfg.Hkv, dcfg.D)
+    t0 = time.perf_counter()
+    oracle.decode_paged(d["q"], d["k_pool"], d["v_pool"], d["page_table"], lens, scale=dcfg.softmax_scale)
+    dt = time.perf_counter() - t0
+    return {"value": round(kv / dt / 1e9, 3), "unit": "GB/s", "cores": oracle.oracle_threads(), "kind": "oracle",
+            "sample": f"all {lens.size} sequences x {dcfg.Hq} heads of the paged-decode workload "
+                      f"({kv:.3e} KV bytes, {dt:.2f} s, FP64)"}
+
+
+def reported_legs(api, up, stream, cpu_seconds=None):
     """Reported (not the headline value): the long-context prefill (B=1,
     S=32768, Q and K drawn x4) and the chunked-prefill replay of 8192 tokens
     in chunks of 2048, 512 and 1.  TFLOP/s from the algorithmic flops of a
@@ -147,23 +207,33 @@ def reported_legs(api, up, stream):
     log("long-context prefill (S=32768)")
     q, k, v = gen.prefill_inputs(cfg5)
     qd, kd, vd = up(q), up(k), up(v)
+    sha = {"q": sha256_of(q), "k": sha256_of(k), "v": sha256_of(v)}
+    cpu5 = None
+    if cpu_seconds:
+        log(f"timing the CPU oracle on the S=32768 workload for ~{cpu_seconds:.0f} s")
+        cpu5 = cpu_baseline(q, k, v, cfg5, cpu_seconds)
     del q, k, v
     ms = timed(lambda: api.prefill(qd, kd, vd, block=cfg5.block), 3)
     res["long_prefill_b1_s32768"] = {"tflops": round(cfg5.flops() / (ms * 1e-3) / 1e12, 2), "ms": round(ms, 4),
-                                     "frac_of_peak": round(cfg5.flops() / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+                                     "frac_of_peak": round(cfg5.flops() / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                                     "input_sha256": sha, "cp_shards": shard_manifest(cfg5),
+                                     "cpu_baseline": cpu5}
     del qd, kd, vd
     torch.cuda.empty_cache()
     cfg3 = gen.CFG3
     q, k, v = gen.prefill_inputs(cfg3)
     qd, kd, vd = up(q), up(k), up(v)
     del q, k, v
+    # one workspace for the chunk-of-one route, sized for the longest call
+    ws1 = api.alloc_workspace(api.decode_workspace_bytes(cfg3.Hq, cfg3.Hkv, cfg3.B, cfg3.S, block=cfg3.block),
+                              qd.device)
     for chunk in (2048, 512, 1):
         log(f"chunked replay, chunk {chunk}")
         parts = [(qd[:, c0:c0 + chunk].contiguous(), c0) for c0 in range(0, cfg3.S, chunk)]
 
         def replay():
             for qc, c0 in parts:
-                api.prefill_chunked(qc, kd, vd, cache_len=c0, block=cfg3.block)
+                api.prefill_chunked(qc, kd, vd, cache_len=c0, block=cfg3.block, workspace=ws1)
 
         ms = timed(replay, 1 if chunk == 1 else 3)
         res[f"chunked_replay_s8192_c{chunk}"] = {"tflops": round(cfg3.flops() / (ms * 1e-3) / 1e12, 2),
@@ -187,7 +257,7 @@ def reported_legs(api, up, stream):
     ms = timed(paged_replay, 3)
     res["paged_replay_s8192_c2048_p16"] = {"tflops": round(cfg3.flops() / (ms * 1e-3) / 1e12, 2), "ms": round(ms, 4),
                                             "calls": len(parts)}
-    del parts, kp, vp, qd, kd, vd
+    del parts, kp, vp, qd, kd, vd, ws1
     torch.cuda.empty_cache()
     return res
 
@@ -204,8 +274,10 @@ def backward_leg(api, cfg, qd, kd, vd, up, stream, steps, cpu_q=None):
     dk = torch.zeros(kd.shape, dtype=torch.float32, device=qd.device)
     dv = torch.zeros(kd.shape, dtype=torch.float32, device=qd.device)
 
+    ws = api.alloc_workspace(api.backward_workspace_bytes(cfg.Hq, cfg.Hkv, cfg.B, cfg.S), qd.device)
+
     def call():
-        api.backward(qd, kd, vd, out, lse, do, scale=cfg.softmax_scale, dq=dq, dk=dk, dv=dv)
+        api.backward(qd, kd, vd, out, lse, do, scale=cfg.softmax_scale, dq=dq, dk=dk, dv=dv, workspace=ws)
 
     for _ in range(2):
         call()
@@ -219,7 +291,7 @@ def backward_leg(api, cfg, qd, kd, vd, up, stream, steps, cpu_q=None):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
     flops = 2.5 * cfg.flops()
-    del do, out, lse, dq, dk, dv
+    del do, out, lse, dq, dk, dv, ws
     torch.cuda.empty_cache()
     res = {"tflops": round(flops / (ms * 1e-3) / 1e12, 2), "ms": round(ms, 4),
            "frac_of_peak": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4), "flop_per_step": flops,
@@ -261,19 +333,20 @@ def lm_head_leg(api, up, stream, reps=5, cpu=False):
     w = torch.from_numpy(w_host).to(stream.device)
     x = up(gen.draw_bf16(1000 * 4 + 11, (T, H)))
     tok = torch.from_numpy(gen.lm_tokens(T, V)).to(stream.device)
-    api.lm_head_logprobs(x, w, tok)
+    ws = api.alloc_workspace(api.lm_head_workspace_bytes(T, V), stream.device)
+    api.lm_head_logprobs(x, w, tok, workspace=ws)
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for _ in range(reps):
-        api.lm_head_logprobs(x, w, tok)
+        api.lm_head_logprobs(x, w, tok, workspace=ws)
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / reps
     flops = 2.0 * T * V * H
     wbytes = V * H * 4
-    del w, tok
+    del w, tok, ws
     torch.cuda.empty_cache()
     res = {"ms": round(ms, 4), "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
            "frac_of_fp32_peak": round(flops / (ms * 1e-3) / 1e12 / PEAK_FP32_TFLOPS, 4),
@@ -299,7 +372,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--decode-steps", type=int, default=10)
+    ap.add_argument("--decode-steps", type=int, default=25)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-reported", action="store_true", help="skip the long-context and chunked-replay legs")
@@ -408,10 +481,16 @@ def main():
     del qd, kd, vd, out
     torch.cuda.empty_cache()
     decode = decode_leg(args, api, d, dcfg, up, dev, stream) if d is not None else None
+    if decode is not None and not args.no_cpu_baseline and args.only is None:
+        log("timing the CPU oracle on the paged-decode workload")
+        decode["cpu_baseline"] = decode_cpu_baseline(d, dcfg)
+        decode["input_sha256"] = {name: sha256_of(d[name]) for name in ("q", "k_pool", "v_pool", "page_table",
+                                                                         "ctx_lens")}
     if args.only == "decode":
         print(json.dumps({"only": "decode", "decode": decode}))
         return
-    reported = None if args.no_reported else reported_legs(api, up, stream)
+    reported = None if args.no_reported else reported_legs(
+        api, up, stream, cpu_seconds=None if args.no_cpu_baseline else min(args.cpu_seconds, 15.0))
     lm_head = None
     if not args.no_reported:
         lm_head = lm_head_leg(api, up, stream, cpu=not args.no_cpu_baseline)
@@ -430,7 +509,19 @@ def main():
         "decode": decode,
         "backward": backward,
         "lm_head_logprobs": lm_head,
-        "invariance": {"batch_alone_vs_batch": drift_batch, "cp2_reversed_arrival": drift_cp},
+        "invariance": {"batch_alone_vs_batch": drift_batch, "cp2_reversed_arrival": drift_cp,
+                       "max_abs_drift": None if drift_batch is None else max(drift_batch, drift_cp)},
+        "provenance": {
+            "core_id": api.core_id(), "commit": git_commit(), "kernel_source_sha256": kernel_source_hash(),
+            "merge_order": "global_block_index", "downcast_at": "final_write", "acc_dtype": "fp32",
+            "split_kv": "fixed 128-key blocks counted from position 0; no data-dependent split (decode: fixed "
+                        "4-block units, per-block states folded in ascending block index)",
+            "fallback": False,
+            "input_sha256": {"q": sha256_of(q), "k": sha256_of(k), "v": sha256_of(v)},
+            "cp_shards": shard_manifest(cfg),
+            "tolerances": {"bf16_out": "|g-o| <= 2e-2 + 1e-2*|o|", "fp32_out_abs": 1e-4, "lse_abs": 1e-4,
+                           "invariance_max_abs": 0.0},
+        },
         "reported": reported,
         "cpu_baseline": base,
     }

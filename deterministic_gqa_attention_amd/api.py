@@ -17,7 +17,7 @@ from ._lib import RLAError, RlaParams, RlaPartials, RlaShard
 
 __all__ = ["RLAError", "core_id", "prefill", "prefill_chunked", "prefill_paged", "emit_partials",
            "merge_states", "decode_paged", "decode_workspace_bytes", "backward", "lm_head_logprobs", "params",
-           "alloc_workspace", "decode_paged_static"]
+           "alloc_workspace", "decode_paged_static", "backward_workspace_bytes", "lm_head_workspace_bytes"]
 
 _OUT_DT = {torch.bfloat16: _lib.RLA_DT_BF16, torch.float32: _lib.RLA_DT_FP32}
 _ORDER = {"global_block_index": _lib.RLA_ORDER_GLOBAL_BLOCK_INDEX, "arrival": _lib.RLA_ORDER_ARRIVAL}
@@ -268,6 +268,15 @@ def merge_states(part_out, part_lse, global_block_index, *, Hq=None, out_dtype=t
     _lib.check(lib.rla_merge_states(ctypes.byref(p), ctypes.byref(parts), out.data_ptr(), lse.data_ptr(),
                                     _stream(part_out.device)))
     return out, lse
+
+
+def backward_workspace_bytes(Hq, Hkv, batch, q_rows) -> int:
+    p = params(Hq, Hkv, block=128)
+    return int(_lib.load().rla_backward_workspace_bytes(ctypes.byref(p), batch, q_rows))
+
+
+def lm_head_workspace_bytes(T, V) -> int:
+    return int(_lib.load().rla_lm_head_workspace_bytes(T, V))
 
 
 def decode_workspace_bytes(Hq, Hkv, batch, max_context_len, *, block, out_dtype=torch.bfloat16) -> int:

@@ -22,7 +22,8 @@
 //           plus its partner lane, then a fixed tree over the sub-tiles
 //   acc_b = MFMA chain over the block's keys from zero, P rounded to bf16
 //           (FP32-output mode: P = hi + lo, two MFMAs per key step)
-//   O_b   = acc_b * (1 / l_b);   L_b = (m_t + log2 l_b) * ln 2
+//   O_b   = acc_b * r_b with r_b = v_rcp_f32(l_b) (within 1 ulp of 1 / l_b);
+//           L_b = (m_t + log2 l_b) * ln 2
 //   empty row (no unmasked key) -> (O_b, L_b) = (0, -inf)
 // Fold over blocks in ascending index from the empty state (m, l, acc) =
 // (-inf, 0, 0), with a lazily moved reference m (tau = 8, natural-log units).
@@ -143,7 +144,7 @@ __device__ __forceinline__ float combine_subtiles(const float* s) {
 
 // Block item scalars from the block max (log2 domain) and block sum.
 struct ItemScalars {
-  float r;    // 1 / l_b, or 0 for an empty row
+  float r;    // v_rcp_f32(l_b) (1 ulp), or 0 for an empty row
   float L;    // natural-log LSE of the block, or -inf for an empty row
 };
 __device__ __forceinline__ ItemScalars item_scalars(float m_t, float l_b) {
@@ -152,7 +153,7 @@ __device__ __forceinline__ ItemScalars item_scalars(float m_t, float l_b) {
     s.r = 0.0f;
     s.L = kNegInf;
   } else {
-    s.r = 1.0f / l_b;
+    s.r = __builtin_amdgcn_rcpf(l_b);
     float lg = hw_log2(l_b);
     float t = m_t + lg;
     s.L = t * kLn2;

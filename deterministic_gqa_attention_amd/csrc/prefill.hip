@@ -67,6 +67,27 @@ __device__ __forceinline__ void block_scores(const char* kreg, const bf16x8 (&qf
   }
 }
 
+// The same one key sub-tile at a time (each sub-tile's chain over the head
+// dimension in the same order, so the same bits), with K fragments read R-1
+// MFMAs ahead through a ring of R registers, from prebuilt fragment addresses.
+template <int BK, int R>
+__device__ __forceinline__ void block_scores_kr(const KReads<BK>& kr, const bf16x8 (&qf)[kDSteps],
+                                                f32x16 (&s)[BK / 32]) {
+  constexpr int NKT = BK / 32;
+  constexpr int N = NKT * kDSteps;
+  bf16x8 kf[R];
+#pragma unroll
+  for (int i = 0; i < R - 1; ++i) kf[i] = kr.frag(i / kDSteps, i % kDSteps);
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const int kt = i / kDSteps;
+    const int ds = i % kDSteps;
+    if (i + R - 1 < N) kf[(i + R - 1) % R] = kr.frag((i + R - 1) / kDSteps, (i + R - 1) % kDSteps);
+    s[kt] = mfma(kf[i % R], qf[ds], ds == 0 ? f32x16{} : s[kt]);
+    sched_fence();
+  }
+}
+
 // The same with the Q B-fragments read from LDS: step ds of this lane at
 // qlane + ds*1024 (the wave's 8 KiB Q tile stored in fragment order).
 template <int BK>
@@ -586,8 +607,16 @@ __global__ __launch_bounds__(kThreads) void prefill_pp_kernel(const PrefillArgs 
   WaveCtx w;
   wave_setup(a, blockIdx.x, w);
   const TileMap& tm = w.tm;
-  const int64_t n_kv_blocks = (a.kv_len + BK - 1) / BK;
-  const int64_t nblk = a.causal ? min(n_kv_blocks, (a.pos0 + tm.tile_t1) / BK + 1) : n_kv_blocks;
+  // 32-bit block indices and positions (the host keeps one head's rows below 2 GiB)
+  const int kvl32 = static_cast<int>(a.kv_len);
+  const int n_kv_blocks = (kvl32 + BK - 1) / BK;
+  const int last_pos = static_cast<int>(a.pos0) + tm.tile_t1;
+  const int nblk = a.causal ? min(n_kv_blocks, last_pos / BK + 1) : n_kv_blocks;
+  const int first_pos = static_cast<int>(a.pos0) + tm.t0;
+  const int wave_last = static_cast<int>(a.pos0) + tm.t_last;
+  // does block j hold a key a row of this wave may see / do all rows see all its keys
+  auto sees = [&](int j) { return tm.wave_has_rows && j * BK < kvl32 && (!a.causal || j * BK <= wave_last); };
+  auto full = [&](int j) { return (j + 1) * BK <= kvl32 && (!a.causal || (j + 1) * BK - 1 <= first_pos); };
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int group = wave >> 2;
 
@@ -607,7 +636,11 @@ __global__ __launch_bounds__(kThreads) void prefill_pp_kernel(const PrefillArgs 
 
   // Loads of half-step 2i (group 1): K_{i+1} into the K array of parity
   // (i+1)&1 and V_i into the V array of parity i&1.  par = i & 1.
-  auto loads = [&](auto par, int64_t i) {
+  // fragment addresses of buffer 0 of each pair, computed once; buffer 1 of a
+  // pair sits at a fixed distance, so every read is one register + immediate
+  const KReads<BK> kr0(kb0, opaque_lane());
+  const VReads<BK> vr0(vb0, opaque_lane());
+  auto loads = [&](auto par, int i) {
     constexpr int p = decltype(par)::value;
     if (i + 1 < nblk) ld.issue_k(p ? kb0 : kb1, w.krs, (i + 1) * BK);
     if (i < nblk) ld.issue_v(p ? vb1 : vb0, w.vrs, i * BK);
@@ -616,15 +649,17 @@ __global__ __launch_bounds__(kThreads) void prefill_pp_kernel(const PrefillArgs 
   // parity (j-1)&1, then the scores of block j from the K array of parity j&1.
   // The matrix stage is the one the SIMD's throughput depends on, so its wave
   // gets the higher issue priority.
-  auto stage_a = [&](auto par, int64_t j, f32x16 (&s)[NKT], const P& pp, const FoldIn& inp) {
+  auto stage_a = [&](auto par, int j, f32x16 (&s)[NKT], const P& pp, const FoldIn& inp) {
     constexpr int p = decltype(par)::value;
-    const char* kc = p ? kb1 : kb0;
-    const char* vp = p ? vb0 : vb1;
+    KReads<BK> kr = kr0;
+    kr.reg = p ? kb1 : kb0;
+    VReads<BK> vr = vr0;
+    vr.reg = p ? vb0 : vb1;
     __builtin_amdgcn_s_setprio(2);
-    if (j > 0 && wave_sees<BK>(a, tm, j - 1)) block_pv_fold<BK, false>(VReads<BK>(vp, opaque_lane()), pp, inp, acc);
+    if (j > 0 && sees(j - 1)) block_pv_fold<BK, false>(vr, pp, inp, acc);
     sched_fence();
-    if (j < nblk && wave_sees<BK>(a, tm, j)) {
-      block_scores<BK>(kc, w.qf, s, opaque_lane());
+    if (j < nblk && sees(j)) {
+      block_scores_kr<BK, 3>(kr, w.qf, s);
     } else {
 #pragma unroll
       for (int kt = 0; kt < NKT; ++kt) s[kt] = f32x16{};  // defined on every path (unused)
@@ -632,13 +667,13 @@ __global__ __launch_bounds__(kThreads) void prefill_pp_kernel(const PrefillArgs 
     __builtin_amdgcn_s_setprio(0);
   };
   // Vector stage B_j: softmax of S_j, fold scalars of block j.
-  auto stage_b = [&](int64_t j, f32x16 (&s)[NKT], P& pn, FoldIn& inn) {
-    if (!wave_sees<BK>(a, tm, j)) {
+  auto stage_b = [&](int j, f32x16 (&s)[NKT], P& pn, FoldIn& inn) {
+    if (!sees(j)) {
       pn = P{};  // defined on every path, so the previous block's P is dead after its PV
       inn = FoldIn{};
       return;
     }
-    block_softmax<BK, false>(s, !wave_full<BK>(a, tm, j), static_cast<int>(j * BK), kvl, a.causal, qpos, a.c, pn);
+    block_softmax<BK, false>(s, !full(j), j * BK, kvl, a.causal, qpos, a.c, pn);
     inn = fold_prepare(fs, pn.m_t, pn.l_b);
   };
   // End of a half-step: (group 1, when it has loads in flight) wait for
@@ -657,7 +692,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pp_kernel(const PrefillArgs 
   FoldIn ib{};   // and its fold scalars
   if (group == 0) {
     lds_barrier();  // prologue: K_0 landed
-    int64_t j = 0;
+    int j = 0;
     for (; j + 2 <= nblk; j += 2) {
       {
         f32x16 s[NKT];
@@ -700,7 +735,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pp_kernel(const PrefillArgs 
     lds_barrier();
     loads(I0{}, 0);
     end_half();  // half-step 0
-    int64_t j = 0;
+    int j = 0;
     for (; j + 2 <= nblk; j += 2) {
       {
         f32x16 s[NKT];

@@ -193,18 +193,29 @@ rla_status run_decode(const rla_attn_params* p, int g, const void* q, const void
   d.len_cap = static_cast<int32_t>(cap);
   d.c = score_scale(p);
   d.unit_blocks = rla::kDecodeUnitBlocks;
-  if (host_context_lens != nullptr || context_lens == nullptr) {
-    // compact grid: exactly the units the lengths need
+  auto units_of = [&](int64_t len) {
+    const int64_t nb = (len + p->kv_block_size - 1) / p->kv_block_size;
+    return (nb + rla::kDecodeUnitBlocks - 1) / rla::kDecodeUnitBlocks;
+  };
+  if (context_lens == nullptr) {
+    // every sequence has uniform_len keys: exactly the units they need
+    d.len_mode = rla::kLensUniform;
+    d.n_units = static_cast<int64_t>(batch) * units_of(std::max<int64_t>(0, std::min<int64_t>(uniform_len, cap)));
+  } else if (host_context_lens != nullptr && batch <= rla::kDecodeTableSeqs) {
+    // the (validated) host lengths and their unit prefix sums travel with the
+    // launches: exactly the units they need, no device length read
+    d.len_mode = rla::kLensTable;
     int64_t units = 0;
     for (int i = 0; i < batch; ++i) {
-      const int64_t len = context_lens == nullptr ? uniform_len : host_context_lens[i];
-      const int64_t nb = (len + p->kv_block_size - 1) / p->kv_block_size;
-      units += (nb + rla::kDecodeUnitBlocks - 1) / rla::kDecodeUnitBlocks;
+      d.lens[i] = host_context_lens[i];
+      d.unit_start[i] = static_cast<int32_t>(units);
+      units += units_of(host_context_lens[i]);
     }
-    d.compact = 1;
+    d.unit_start[batch] = static_cast<int32_t>(units);
     d.n_units = units;
   } else {
-    d.compact = 0;
+    // device lengths: every unit up to max_context_len, idle ones exit
+    d.len_mode = rla::kLensDevice;
     d.n_units = static_cast<int64_t>(batch) * ((max_blocks + rla::kDecodeUnitBlocks - 1) / rla::kDecodeUnitBlocks);
   }
   const bool f32 = p->out_dtype == RLA_DT_FP32;
@@ -217,6 +228,8 @@ rla_status run_decode(const rla_attn_params* p, int g, const void* q, const void
   f.part_lse = items_lse;
   f.ctx_lens = context_lens;
   f.uniform_len = uniform_len;
+  f.len_mode = d.len_mode;
+  if (d.len_mode == rla::kLensTable) std::memcpy(f.lens, d.lens, sizeof(int32_t) * batch);
   f.out = out;
   f.lse = lse;
   f.rows = batch;
@@ -250,8 +263,9 @@ rla_status validate_decode(const rla_attn_params* p, const void* q, const void* 
   if (q == nullptr || k_pool == nullptr || v_pool == nullptr || page_table == nullptr ||
       context_lens == nullptr || out == nullptr || lse == nullptr)
     return fail(RLA_ERR_NULL_POINTER, "a required pointer is NULL");
-  if (batch < 1 || max_context_len < 0 || num_pages < 1 || page_size < 1 || max_pages_per_seq < 1)
-    return fail(RLA_ERR_BAD_SHAPE, "need batch>=1, max_context_len>=0, num_pages>=1, page_size>=1, "
+  if (batch < 1 || max_context_len < 0 || max_context_len > (1 << 30) || num_pages < 1 || page_size < 1 ||
+      max_pages_per_seq < 1)
+    return fail(RLA_ERR_BAD_SHAPE, "need batch>=1, 0<=max_context_len<=2^30, num_pages>=1, page_size>=1, "
                 "max_pages_per_seq>=1");
   if (p->kv_block_size % page_size != 0)
     return fail(RLA_ERR_UNSUPPORTED, "page_size=%d must divide kv_block_size=%d", page_size, p->kv_block_size);

@@ -106,66 +106,60 @@ struct BlockRegs {
   }
 };
 
-__device__ __forceinline__ int64_t clamp_len(const DecodeArgs& a, int seq) {
-  int64_t len = a.ctx_lens != nullptr ? a.ctx_lens[seq] : a.uniform_len;
+__device__ __forceinline__ int clamp_len(const DecodeArgs& a, int seq) {
+  const int len = a.len_mode == kLensDevice ? a.ctx_lens[seq] : a.uniform_len;
   return len < 0 ? 0 : (len > a.len_cap ? a.len_cap : len);
 }
 
-// Map a unit index to (sequence, first block, block count).  Compact grids
-// walk the sequences in order (lane-parallel prefix sum of units per
-// sequence, 64 sequences per step); otherwise unit u is unit u / Bd of
-// sequence u % Bd.  Returns false for an idle unit.
+// Map a unit index to (sequence, first block, block count); false for an
+// idle unit.  kLensTable: the sequence is the last one whose first unit
+// (unit_start, a prefix sum the host built from the lengths) is <= u, found by
+// a binary search over the launch arguments, so no workgroup waits on a
+// device-memory read before its first KV load.  kLensUniform: every sequence
+// has the same number of units.  kLensDevice: unit u is unit u / Bd of
+// sequence u % Bd (the grid covers max_context_len; units past a sequence's
+// length are idle).
 template <int BK>
-__device__ __forceinline__ bool locate_unit(const DecodeArgs& a, int64_t u, int& seq, int64_t& blk0, int64_t& blk1,
-                                            int64_t& len) {
+__device__ __forceinline__ bool locate_unit(const DecodeArgs& a, uint32_t u, int& seq, int& blk0, int& blk1, int& len) {
   const int U = a.unit_blocks;
-  if (!a.compact) {
-    seq = static_cast<int>(u % a.Bd);
+  uint32_t k;  // unit index within the sequence
+  if (a.len_mode == kLensTable) {
+    int lo = 0, hi = a.Bd;  // unit_start[lo] <= u < unit_start[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (static_cast<uint32_t>(a.unit_start[mid]) <= u) {
+        lo = mid;
+      } else {
+        hi = mid;
+      }
+    }
+    seq = lo;
+    len = a.lens[lo];
+    k = u - a.unit_start[lo];
+  } else if (a.len_mode == kLensUniform) {
+    len = clamp_len(a, 0);
+    const uint32_t per = static_cast<uint32_t>(((len + BK - 1) / BK + U - 1) / U);  // len >= 0
+    if (per == 0) return false;
+    seq = static_cast<int>(u / per);
+    k = u - static_cast<uint32_t>(seq) * per;
+  } else {
+    const uint32_t bd = static_cast<uint32_t>(a.Bd);
+    seq = static_cast<int>(u % bd);
     len = clamp_len(a, seq);
-    const int64_t nb = (len + BK - 1) / BK;
-    blk0 = (u / a.Bd) * U;
-    blk1 = min(blk0 + U, nb);
-    return blk0 < nb;
+    k = u / bd;
   }
-  const int lane = threadIdx.x & 63;
-  int64_t before = 0;  // units of the sequences already passed
-  for (int s0 = 0; s0 < a.Bd; s0 += 64) {
-    const int s = s0 + lane;
-    int64_t nu = 0;
-    if (s < a.Bd) {
-      const int64_t l = clamp_len(a, s);
-      nu = ((l + BK - 1) / BK + U - 1) / U;
-    }
-    int64_t incl = nu;  // inclusive prefix sum over the 64 lanes
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int64_t y = __shfl_up(incl, o, 64);
-      if (lane >= o) incl += y;
-    }
-    const int64_t total = __shfl(incl, 63, 64);
-    if (u < before + total) {
-      // first lane whose inclusive sum exceeds u - before
-      const unsigned long long m = __ballot(incl > u - before);
-      const int hit = __ffsll(static_cast<long long>(m)) - 1;
-      const int64_t excl = __shfl(incl - nu, hit, 64);
-      seq = s0 + hit;
-      len = clamp_len(a, seq);
-      const int64_t nb = (len + BK - 1) / BK;
-      blk0 = (u - before - excl) * U;
-      blk1 = min(blk0 + U, nb);
-      return blk0 < nb;
-    }
-    before += total;
-  }
-  return false;
+  const int nb = (len + BK - 1) / BK;
+  blk0 = static_cast<int>(k) * U;
+  blk1 = min(blk0 + U, nb);
+  return blk0 < nb;
 }
 
 // One block's partial states for the group's heads, from the K fragments in
 // registers (waves < NKT) and the V tile in LDS.
 template <int BK, bool F32>
 __device__ __forceinline__ void decode_block(const DecodeArgs& a, char* lds, BlockRegs<BK>& br,
-                                             const bf16x8 (&qf)[kDSteps], int seq, int hk, int64_t blk,
-                                             int64_t len, const UnitPages& up, int next_key0) {
+                                             const bf16x8 (&qf)[kDSteps], int seq, int hk, int blk, int len,
+                                             const UnitPages& up, int next_key0) {
   using Lay = DecodeLds<BK, F32>;
   constexpr int NKT = Lay::NKT;
   const char* lv = lds + Lay::kVOff;  // V rows at lv + TileLayout::v_rel(...)
@@ -177,7 +171,7 @@ __device__ __forceinline__ void decode_block(const DecodeArgs& a, char* lds, Blo
   const int lane = tid & 63;
   const int col = lane & 31;
   const int half = lane >> 5;
-  const int64_t key0 = blk * BK;
+  const int key0 = blk * BK;
 
   // ---- scores of sub-tile kt = wave (waves < NKT)
   f32x16 s = f32x16{};
@@ -187,12 +181,12 @@ __device__ __forceinline__ void decode_block(const DecodeArgs& a, char* lds, Blo
     // K of the block two ahead, into the registers the MFMAs just read (the
     // fp32-output instance, short of registers, loads it after the block)
     if constexpr (!F32) {
-      if (next_key0 >= 0) br.load_k(a, up, hk, next_key0, static_cast<int>(len));
+      if (next_key0 >= 0) br.load_k(a, up, hk, next_key0, len);
     }
     float m_lane = kNegInf;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      const int64_t kk = key0 + wave * 32 + acc_row(v, half);
+      const int kk = key0 + wave * 32 + acc_row(v, half);
       const float d = kk < len ? s[v] : kNegInf;
       s[v] = d;
       m_lane = fmaxf(m_lane, d);
@@ -268,7 +262,7 @@ __device__ __forceinline__ void decode_block(const DecodeArgs& a, char* lds, Blo
     if (wave == 0 && half == 0) a.items_lse[item] = sc.L;
   }
   if constexpr (F32) {
-    if (next_key0 >= 0) br.load_k(a, up, hk, next_key0, static_cast<int>(len));
+    if (next_key0 >= 0) br.load_k(a, up, hk, next_key0, len);
   }
 }
 
@@ -281,11 +275,12 @@ __global__ __launch_bounds__(kThreads, 2) void decode_items_kernel(const DecodeA
   __shared__ __attribute__((aligned(16))) char lds[Lay::kBytes];
   char* lv = lds + Lay::kVOff;
 
-  const int64_t x = blockIdx.x;
-  const int hk = static_cast<int>(x % a.Hkv);
+  const uint32_t x = blockIdx.x;
+  const uint32_t hkv = static_cast<uint32_t>(a.Hkv);
+  const int hk = static_cast<int>(x % hkv);
   int seq;
-  int64_t blk0, blk1, len;
-  if (!locate_unit<BK>(a, x / a.Hkv, seq, blk0, blk1, len)) return;  // uniform across the workgroup
+  int blk0, blk1, len;
+  if (!locate_unit<BK>(a, x / hkv, seq, blk0, blk1, len)) return;  // uniform across the workgroup
 
   const int lane = threadIdx.x & 63;
   const int col = lane & 31;
@@ -296,20 +291,19 @@ __global__ __launch_bounds__(kThreads, 2) void decode_items_kernel(const DecodeA
   {
     int32_t* ids = reinterpret_cast<int32_t*>(lds + Lay::kPageOff);
     up.ids = ids;
-    up.first = static_cast<int>((blk0 * BK) >> a.log2_P);
-    const int64_t kend = blk1 * BK < len ? blk1 * BK : len;
-    const int64_t count = (kend + a.P - 1) / a.P - up.first;
+    up.first = (blk0 * BK) >> a.log2_P;
+    const int kend = min(blk1 * BK, len);
+    const int count = ((kend + a.P - 1) >> a.log2_P) - up.first;
     const int32_t* row = a.page_table + static_cast<int64_t>(seq) * a.max_pages + up.first;
     const int32_t id0 = seq * a.max_pages + up.first;  // no table: page i of sequence s is s*max_pages + i
-    for (int64_t t = threadIdx.x; t < count; t += kThreads)
+    for (int t = threadIdx.x; t < count; t += kThreads)
       ids[t] = a.page_table != nullptr ? row[t] : id0 + static_cast<int32_t>(t);
     __syncthreads();
   }
 
   BlockRegs<BK> r0, r1;
-  const int ilen = static_cast<int>(len);
-  r0.load(a, up, hk, static_cast<int>(blk0 * BK), ilen);
-  if (blk0 + 1 < blk1) r1.load(a, up, hk, static_cast<int>((blk0 + 1) * BK), ilen);
+  r0.load(a, up, hk, blk0 * BK, len);
+  if (blk0 + 1 < blk1) r1.load(a, up, hk, (blk0 + 1) * BK, len);
 
   // Q fragments of the group's heads (columns >= G are zero)
   bf16x8 qf[kDSteps];
@@ -320,17 +314,17 @@ __global__ __launch_bounds__(kThreads, 2) void decode_items_kernel(const DecodeA
     for (int ds = 0; ds < kDSteps; ++ds) qf[ds] = as_bf16x8(qok ? gload16(qrow + 16 * ds) : u32x4{0, 0, 0, 0});
   }
 
-  for (int64_t blk = blk0; blk < blk1; blk += 2) {
-    const int n0 = blk + 2 < blk1 ? static_cast<int>((blk + 2) * BK) : -1;
+  for (int blk = blk0; blk < blk1; blk += 2) {
+    const int n0 = blk + 2 < blk1 ? (blk + 2) * BK : -1;
     r0.store_v(lv);
-    if (n0 >= 0) r0.load_v(a, up, hk, n0, ilen);
+    if (n0 >= 0) r0.load_v(a, up, hk, n0, len);
     lds_barrier();  // V of blk visible
     decode_block<BK, F32>(a, lds, r0, qf, seq, hk, blk, len, up, n0);
     lds_barrier();  // everyone done with V / P of blk
     if (blk + 1 < blk1) {
-      const int n1 = blk + 3 < blk1 ? static_cast<int>((blk + 3) * BK) : -1;
+      const int n1 = blk + 3 < blk1 ? (blk + 3) * BK : -1;
       r1.store_v(lv);
-      if (n1 >= 0) r1.load_v(a, up, hk, n1, ilen);
+      if (n1 >= 0) r1.load_v(a, up, hk, n1, len);
       lds_barrier();
       decode_block<BK, F32>(a, lds, r1, qf, seq, hk, blk + 1, len, up, n1);
       lds_barrier();

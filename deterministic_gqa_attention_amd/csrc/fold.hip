@@ -30,7 +30,9 @@ __global__ __launch_bounds__(kThreads) void fold_kernel(const FoldArgs a) {
 
   int n;
   if constexpr (DECODE) {
-    int64_t len = a.ctx_lens != nullptr ? a.ctx_lens[row] : a.uniform_len;
+    int64_t len = a.uniform_len;
+    if (a.len_mode == kLensTable) len = a.lens[row];
+    if (a.len_mode == kLensDevice) len = a.ctx_lens[row];
     len = len < 0 ? 0 : (len > a.len_cap ? a.len_cap : len);
     n = static_cast<int>((len + a.block - 1) / a.block);
   } else {

@@ -43,27 +43,38 @@ struct PrefillArgs {
   uint16_t emit_blocks[kMaxParts];
 };
 
+// Sequences whose lengths (and unit prefix sums) travel with the decode
+// launches instead of being read from device memory.
+constexpr int kDecodeTableSeqs = 256;
+
+// How a decode launch finds each sequence's length and each workgroup's unit.
+enum DecodeLenMode : int32_t {
+  kLensDevice = 0,   // ctx_lens in device memory; grid Bd x max_units, idle units exit
+  kLensUniform = 1,  // every sequence has uniform_len keys; grid of exactly the units needed
+  kLensTable = 2,    // lens[] / unit_start[] below; grid of exactly the units needed
+};
+
 // Paged decode, pass 1: one workgroup per (kv head, unit of up to
 // unit_blocks consecutive KV blocks of one sequence) writes each block's
-// partial state for the group's q heads.  compact = 1: the grid enumerates
-// exactly the units the context lengths need (found by a prefix scan of the
-// lengths); compact = 0: the grid is Bd x max_units and idle units exit.
+// partial state for the group's q heads.
 struct DecodeArgs {
   const uint16_t* q;          // [Bd][Hq][D]
   const uint16_t* k_pool;     // [num_pages][Hkv][P][D]
   const uint16_t* v_pool;
   const int32_t* page_table;  // [Bd][max_pages]; null: page i of sequence s is s*max_pages + i
-  const int32_t* ctx_lens;    // [Bd]; null: every sequence has uniform_len keys
+  const int32_t* ctx_lens;    // [Bd] (kLensDevice only)
   float* items_out;           // [Bd][max_blocks][Hq][D]
   float* items_lse;           // [Bd][max_blocks][Hq]
   int64_t num_pages;
   int32_t P, max_pages, Bd, Hq, Hkv, G, max_blocks, len_cap;
   int32_t log2_P;             // page size is a power of two (it divides the block)
   int32_t unit_blocks;        // KV blocks per workgroup unit
-  int32_t compact;
+  int32_t len_mode;           // DecodeLenMode
   int64_t n_units;            // units in the grid (per kv head)
-  int32_t uniform_len;        // context length of every sequence when ctx_lens is null
+  int32_t uniform_len;        // kLensUniform: context length of every sequence
   float c;
+  int32_t lens[kDecodeTableSeqs];            // kLensTable: length of sequence s (validated, <= len_cap)
+  int32_t unit_start[kDecodeTableSeqs + 1];  // kLensTable: first unit of sequence s; [Bd] = n_units
 };
 
 // Fold of per-block partial states in ascending block order (decode pass 2)
@@ -71,8 +82,9 @@ struct DecodeArgs {
 struct FoldArgs {
   const float* part_out;      // merge: [n_parts][rows][Hq][D]; decode: items
   const float* part_lse;
-  const int32_t* ctx_lens;    // decode: [Bd] (block count per row), null: uniform_len; merge: null
-  int32_t uniform_len;        // decode: length of every row when ctx_lens is null
+  const int32_t* ctx_lens;    // decode, kLensDevice: [Bd] (block count per row); merge: null
+  int32_t uniform_len;        // decode, kLensUniform: length of every row
+  int32_t len_mode;           // decode: DecodeLenMode (kLensTable: lens[] below)
   void* out;                  // [rows][Hq][D] bf16 or fp32
   float* lse;                 // [rows][Hq]
   int64_t rows;
@@ -81,6 +93,7 @@ struct FoldArgs {
   int32_t block;              // decode: keys per block; merge: unused
   int32_t len_cap;            // decode: clamp on context lengths
   uint16_t order[kMaxParts];  // merge: part indices in fold order
+  int32_t lens[kDecodeTableSeqs];  // decode, kLensTable: length of row s
 };
 
 // Backward (dQ, dK, dV of Out).  Query row t of batch b sits at position

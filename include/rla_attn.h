@@ -185,14 +185,14 @@ rla_status rla_attn_prefill_paged(const rla_attn_params* p, const void* q_chunk,
  * q [batch][Hq][128]; k_pool, v_pool [num_pages][Hkv][page_size][128] bf16;
  * page_table [batch][max_pages_per_seq] int32 (device); context_lens [batch]
  * int32 (device).  host_context_lens [host][batch] may be NULL; when given it
- * must hold the same lengths as context_lens (the launch is sized from the host
- * copy and the kernels read the device copy, so a device length above its host
- * length leaves blocks uncomputed: unspecified result).  The host lengths are
- * validated against max_context_len and the table width before anything is
- * enqueued and the launch covers exactly the blocks they need; without them
- * the launch covers every block up to max_context_len and idle workgroups exit
- * (the results are the same bits either way).  page_size must divide
- * kv_block_size.  Lengths above
+ * must hold the same lengths as context_lens.  It is validated against
+ * max_context_len and the table width before anything is enqueued, and for
+ * batch <= 256 the kernels take every length from it (the lengths and the
+ * per-sequence workgroup offsets travel with the launches, context_lens is not
+ * read) and cover exactly the blocks it needs.  Without it, or above 256
+ * sequences, the kernels read context_lens and the launch covers every block
+ * up to max_context_len, idle workgroups exiting.  The results are the same
+ * bits either way.  page_size must divide kv_block_size.  Lengths above
  * min(max_context_len, max_pages_per_seq*page_size) are clamped to it, and a
  * page id outside [0, num_pages) is clamped into that range before use, so a
  * bad table cannot fault, but its result is unspecified.

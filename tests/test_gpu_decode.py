@@ -182,3 +182,44 @@ def test_paged_decode_64_seqs_full():
     o2, l2 = _decode(r, cfg, block=cfg.block)
     assert_bitwise(o2, out, "relocated Out")
     assert_bitwise(l2, lse, "relocated LSE")
+
+
+# Empty sequences at the start, in the middle and at the end of the batch.
+EMPTY_LENS = np.array([0, 5, 0, 0, 700, 129, 0], np.int32)
+
+
+@pytest.mark.parametrize("block", [64, 128])
+def test_length_sources_and_empty_sequences(block):
+    """The lengths reach the kernels either with the launch (host lengths, up
+    to 256 sequences) or from device memory; both give the same bits, and an
+    empty sequence gives Out = 0 and LSE = -inf."""
+    d = gen.decode_inputs(SMALL, lengths=EMPTY_LENS)
+    say(f"[decode] length sources, empty sequences, block={block}")
+    a_o, a_l = _decode(d, SMALL, block=block, out_dtype=torch.float32)
+    b_o, b_l = _decode(d, SMALL, block=block, out_dtype=torch.float32, host_lens=False)
+    assert_bitwise(b_o, a_o, "Out, device lengths")
+    assert_bitwise(b_l, a_l, "LSE, device lengths")
+    empty = torch.from_numpy(EMPTY_LENS == 0).to(a_o.device)
+    assert not a_o[empty].any(), "empty sequence Out not zero"
+    assert bool(torch.isneginf(a_l[empty]).all()), "empty sequence LSE not -inf"
+    ro, rl = oracle.decode_paged(d["q"], d["k_pool"], d["v_pool"], d["page_table"], d["ctx_lens"],
+                                 scale=SMALL.softmax_scale)
+    live = EMPTY_LENS > 0
+    check_parity(host_f64(a_o)[live], host_f64(a_l)[live], ro[live], rl[live], f32_out=True,
+                 what="decode with empty sequences")
+
+
+def test_more_sequences_than_the_launch_table():
+    """300 sequences (above the 256 whose lengths travel with the launch):
+    with host lengths the kernels read the device lengths; every sequence's
+    bits equal those of a batch small enough for the launch table."""
+    lens = (np.arange(300, dtype=np.int32) * 37) % 400 + 1
+    cfg = gen.DecodeConfig(47, "decode, 300 sequences", batch=300, Hq=8, Hkv=2, D=128, page_size=16,
+                           num_pages=8192, len_lo=1, len_hi=400, block=128)
+    d = gen.decode_inputs(cfg, lengths=lens)
+    say("[decode] 300 sequences")
+    big_o, big_l = _decode(d, cfg, block=128)
+    for seqs in (np.arange(0, 150), np.arange(150, 300)):
+        o, l = _decode(d, cfg, block=128, seqs=seqs)
+        assert_bitwise(o, big_o[seqs[0]:seqs[-1] + 1], f"Out of sequences {seqs[0]}..{seqs[-1]}")
+        assert_bitwise(l, big_l[seqs[0]:seqs[-1] + 1], f"LSE of sequences {seqs[0]}..{seqs[-1]}")

@@ -193,30 +193,36 @@ rla_status run_decode(const rla_attn_params* p, int g, const void* q, const void
   d.len_cap = static_cast<int32_t>(cap);
   d.c = score_scale(p);
   d.unit_blocks = rla::kDecodeUnitBlocks;
-  auto units_of = [&](int64_t len) {
+  // Head units fold up to 64 blocks each (fewer where the unit's page ids
+  // would not fit the workgroup's staging area: small pages).
+  d.head_blocks = static_cast<int32_t>(std::min<int64_t>(
+      64, static_cast<int64_t>(rla::kDecodeIdsCap) * page_size / p->kv_block_size));
+  d.out = out;
+  d.lse = lse;
+  auto tails_of = [&](int64_t len) {
     const int64_t nb = (len + p->kv_block_size - 1) / p->kv_block_size;
-    return (nb + rla::kDecodeUnitBlocks - 1) / rla::kDecodeUnitBlocks;
+    return nb > d.head_blocks ? (nb - d.head_blocks + rla::kDecodeUnitBlocks - 1) / rla::kDecodeUnitBlocks : 0;
   };
   if (context_lens == nullptr) {
-    // every sequence has uniform_len keys: exactly the units they need
+    // every sequence has uniform_len keys: one head and the same tails each
     d.len_mode = rla::kLensUniform;
-    d.n_units = static_cast<int64_t>(batch) * units_of(std::max<int64_t>(0, std::min<int64_t>(uniform_len, cap)));
+    d.n_units = static_cast<int64_t>(batch) * (1 + tails_of(std::max<int64_t>(0, std::min<int64_t>(uniform_len, cap))));
   } else if (host_context_lens != nullptr && batch <= rla::kDecodeTableSeqs) {
-    // the (validated) host lengths and their unit prefix sums travel with the
+    // the (validated) host lengths and the tail prefix sums travel with the
     // launches: exactly the units they need, no device length read
     d.len_mode = rla::kLensTable;
-    int64_t units = 0;
+    int64_t tails = 0;
     for (int i = 0; i < batch; ++i) {
       d.lens[i] = host_context_lens[i];
-      d.unit_start[i] = static_cast<int32_t>(units);
-      units += units_of(host_context_lens[i]);
+      d.unit_start[i] = static_cast<int32_t>(tails);
+      tails += tails_of(host_context_lens[i]);
     }
-    d.unit_start[batch] = static_cast<int32_t>(units);
-    d.n_units = units;
+    d.unit_start[batch] = static_cast<int32_t>(tails);
+    d.n_units = batch + tails;
   } else {
     // device lengths: every unit up to max_context_len, idle ones exit
     d.len_mode = rla::kLensDevice;
-    d.n_units = static_cast<int64_t>(batch) * ((max_blocks + rla::kDecodeUnitBlocks - 1) / rla::kDecodeUnitBlocks);
+    d.n_units = static_cast<int64_t>(batch) * (1 + tails_of(max_context_len));
   }
   const bool f32 = p->out_dtype == RLA_DT_FP32;
   hipError_t e = rla::launch_decode_items(d, p->kv_block_size, f32, s);
@@ -229,6 +235,7 @@ rla_status run_decode(const rla_attn_params* p, int g, const void* q, const void
   f.ctx_lens = context_lens;
   f.uniform_len = uniform_len;
   f.len_mode = d.len_mode;
+  f.head_blocks = d.head_blocks;
   if (d.len_mode == rla::kLensTable) std::memcpy(f.lens, d.lens, sizeof(int32_t) * batch);
   f.out = out;
   f.lse = lse;

@@ -1,9 +1,16 @@
 // Paged-KV decode, pass 1 (gfx950): one workgroup per (kv head, unit of
 // consecutive KV blocks of one sequence) computes each block's partial state
-// for the q heads of the group and writes it to the caller's workspace; pass 2
-// (fold.hip) folds the items of each row in ascending block index.  The cut
-// into units is fixed by the lengths alone and never changes what any item
-// holds.  Decode is bound by reading the KV cache, so each workgroup keeps two
+// for the q heads of the group.  A sequence's head unit (its first 64 blocks
+// or fewer) folds those states in registers, in block order from the empty
+// state, with the fold pass's own steps, and writes the finished row (when it
+// covers the sequence) or its running state; the tail units write every
+// block's state to the caller's workspace, and pass 2 (fold.hip) continues the
+// fold from the head's state over them in ascending block index.  Folding in
+// the head unit saves most of the item writes (which cost far more than their
+// share of the bytes) and most of the per-workgroup set-up.  The cut into
+// units is fixed by the lengths alone and never changes what any block's state
+// holds or the order it is folded in.  Decode is bound by reading the KV
+// cache, so each workgroup keeps two
 // register sets of blocks (K as MFMA A-fragments, V rows bound for LDS) and
 // refills a set with the block two ahead as soon as its registers are free:
 // V right after it is staged in LDS, K right after the score MFMAs have read
@@ -31,7 +38,7 @@ template <int BK, bool F32>
 struct DecodeLds {
   static constexpr int NKT = BK / 32;
   static constexpr int kPBytesPerTile = 64 * 32 * (F32 ? 2 : 1);  // 64 lanes x 16 bf16 (x2 hi/lo)
-  static constexpr int kMaxUnitPages = kDecodeUnitBlocks * BK;     // page ids of one unit (page size >= 1)
+  static constexpr int kMaxUnitPages = kDecodeIdsCap;              // page ids of one unit
   static constexpr int kVOff = 0;                                 // V region only (no K in LDS)
   static constexpr int kPOff = TileLayout<BK>::kVBytes;
   static constexpr int kMaxOff = kPOff + NKT * kPBytesPerTile;
@@ -111,55 +118,81 @@ __device__ __forceinline__ int clamp_len(const DecodeArgs& a, int seq) {
   return len < 0 ? 0 : (len > a.len_cap ? a.len_cap : len);
 }
 
-// Map a unit index to (sequence, first block, block count); false for an
-// idle unit.  kLensTable: the sequence is the last one whose first unit
-// (unit_start, a prefix sum the host built from the lengths) is <= u, found by
-// a binary search over the launch arguments, so no workgroup waits on a
-// device-memory read before its first KV load.  kLensUniform: every sequence
-// has the same number of units.  kLensDevice: unit u is unit u / Bd of
-// sequence u % Bd (the grid covers max_context_len; units past a sequence's
-// length are idle).
+// Map a unit index to (sequence, first block, end block, head or tail);
+// false for an idle unit.  Units [0, Bd) are the sequences' head units,
+// blocks [0, min(nb, head_blocks)); the rest are tail units of up to
+// unit_blocks blocks from head_blocks on.  kLensTable: a tail's sequence is
+// the last one whose first tail unit (unit_start, a prefix sum the host built
+// from the lengths) is <= its index, found by a binary search over the launch
+// arguments, so no workgroup waits on a device-memory read before its first
+// KV load.  kLensUniform: every sequence has the same number of tails.
+// kLensDevice: tail t is tail t / Bd of sequence t % Bd (the grid covers
+// max_context_len; tails past a sequence's length are idle).
 template <int BK>
-__device__ __forceinline__ bool locate_unit(const DecodeArgs& a, uint32_t u, int& seq, int& blk0, int& blk1, int& len) {
+__device__ __forceinline__ bool locate_unit(const DecodeArgs& a, uint32_t u, int& seq, int& blk0, int& blk1, int& len,
+                                            bool& head) {
   const int U = a.unit_blocks;
-  uint32_t k;  // unit index within the sequence
-  if (a.len_mode == kLensTable) {
-    int lo = 0, hi = a.Bd;  // unit_start[lo] <= u < unit_start[hi]
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (static_cast<uint32_t>(a.unit_start[mid]) <= u) {
-        lo = mid;
-      } else {
-        hi = mid;
-      }
-    }
-    seq = lo;
-    len = a.lens[lo];
-    k = u - a.unit_start[lo];
-  } else if (a.len_mode == kLensUniform) {
-    len = clamp_len(a, 0);
-    const uint32_t per = static_cast<uint32_t>(((len + BK - 1) / BK + U - 1) / U);  // len >= 0
-    if (per == 0) return false;
-    seq = static_cast<int>(u / per);
-    k = u - static_cast<uint32_t>(seq) * per;
+  const int H = a.head_blocks;
+  const uint32_t bd = static_cast<uint32_t>(a.Bd);
+  head = u < bd;
+  uint32_t k = 0;  // tail index within the sequence
+  if (head) {
+    seq = static_cast<int>(u);
+    len = a.len_mode == kLensTable ? a.lens[seq] : clamp_len(a, seq);
   } else {
-    const uint32_t bd = static_cast<uint32_t>(a.Bd);
-    seq = static_cast<int>(u % bd);
-    len = clamp_len(a, seq);
-    k = u / bd;
+    const uint32_t t = u - bd;
+    if (a.len_mode == kLensTable) {
+      int lo = 0, hi = a.Bd;  // unit_start[lo] <= t < unit_start[hi]
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (static_cast<uint32_t>(a.unit_start[mid]) <= t) {
+          lo = mid;
+        } else {
+          hi = mid;
+        }
+      }
+      seq = lo;
+      len = a.lens[lo];
+      k = t - static_cast<uint32_t>(a.unit_start[lo]);
+    } else if (a.len_mode == kLensUniform) {
+      len = clamp_len(a, 0);
+      const int nb = (len + BK - 1) / BK;
+      const uint32_t per = static_cast<uint32_t>(nb > H ? (nb - H + U - 1) / U : 0);
+      if (per == 0) return false;
+      seq = static_cast<int>(t / per);
+      k = t - static_cast<uint32_t>(seq) * per;
+    } else {
+      seq = static_cast<int>(t % bd);
+      len = clamp_len(a, seq);
+      k = t / bd;
+    }
   }
   const int nb = (len + BK - 1) / BK;
-  blk0 = static_cast<int>(k) * U;
-  blk1 = min(blk0 + U, nb);
-  return blk0 < nb;
+  if (head) {
+    blk0 = 0;
+    blk1 = min(nb, H);
+  } else {
+    blk0 = H + static_cast<int>(k) * U;
+    blk1 = min(blk0 + U, nb);
+  }
+  return blk0 < blk1;
 }
 
+// Running fold of a head unit, per lane: the state of the lane's column
+// (q head) and the accumulator of its 16 output elements.
+struct HeadFold {
+  FoldState st;
+  float acc[16];
+};
+
 // One block's partial states for the group's heads, from the K fragments in
-// registers (waves < NKT) and the V tile in LDS.
+// registers (waves < NKT) and the V tile in LDS.  A head unit folds them into
+// hf (the fold pass's scalar and element steps, in block order); a tail unit
+// writes them to the items.
 template <int BK, bool F32>
 __device__ __forceinline__ void decode_block(const DecodeArgs& a, char* lds, BlockRegs<BK>& br,
                                              const bf16x8 (&qf)[kDSteps], int seq, int hk, int blk, int len,
-                                             const UnitPages& up, int next_key0) {
+                                             const UnitPages& up, int next_key0, bool head, HeadFold& hf) {
   using Lay = DecodeLds<BK, F32>;
   constexpr int NKT = Lay::NKT;
   const char* lv = lds + Lay::kVOff;  // V rows at lv + TileLayout::v_rel(...)
@@ -249,7 +282,11 @@ __device__ __forceinline__ void decode_block(const DecodeArgs& a, char* lds, Blo
     }
   }
   const ItemScalars sc = item_scalars(m_t, l_b);
-  if (col < a.G) {
+  if (head) {
+    const FoldStep f = fold_scalars(hf.st, sc.L);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) hf.acc[i] = fold_elem(f, hf.acc[i], item_out(acc[i], sc));
+  } else if (col < a.G) {
     const int head = hk * a.G + col;
     const int64_t item = (static_cast<int64_t>(seq) * a.max_blocks + blk) * a.Hq + head;
     float* po = a.items_out + item * kHeadDim;
@@ -280,7 +317,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_items_kernel(const DecodeA
   const int hk = static_cast<int>(x % hkv);
   int seq;
   int blk0, blk1, len;
-  if (!locate_unit<BK>(a, x / hkv, seq, blk0, blk1, len)) return;  // uniform across the workgroup
+  bool head;
+  if (!locate_unit<BK>(a, x / hkv, seq, blk0, blk1, len, head)) return;  // uniform across the workgroup
 
   const int lane = threadIdx.x & 63;
   const int col = lane & 31;
@@ -314,20 +352,63 @@ __global__ __launch_bounds__(kThreads, 2) void decode_items_kernel(const DecodeA
     for (int ds = 0; ds < kDSteps; ++ds) qf[ds] = as_bf16x8(qok ? gload16(qrow + 16 * ds) : u32x4{0, 0, 0, 0});
   }
 
+  HeadFold hf;
+  hf.st = FoldState{kNegInf, 0.0f};
+#pragma unroll
+  for (int i = 0; i < 16; ++i) hf.acc[i] = 0.0f;
+
   for (int blk = blk0; blk < blk1; blk += 2) {
     const int n0 = blk + 2 < blk1 ? (blk + 2) * BK : -1;
     r0.store_v(lv);
     if (n0 >= 0) r0.load_v(a, up, hk, n0, len);
     lds_barrier();  // V of blk visible
-    decode_block<BK, F32>(a, lds, r0, qf, seq, hk, blk, len, up, n0);
+    decode_block<BK, F32>(a, lds, r0, qf, seq, hk, blk, len, up, n0, head, hf);
     lds_barrier();  // everyone done with V / P of blk
     if (blk + 1 < blk1) {
       const int n1 = blk + 3 < blk1 ? (blk + 3) * BK : -1;
       r1.store_v(lv);
       if (n1 >= 0) r1.load_v(a, up, hk, n1, len);
       lds_barrier();
-      decode_block<BK, F32>(a, lds, r1, qf, seq, hk, blk + 1, len, up, n1);
+      decode_block<BK, F32>(a, lds, r1, qf, seq, hk, blk + 1, len, up, n1, head, hf);
       lds_barrier();
+    }
+  }
+
+  // A head unit that covers its sequence finalizes it as the fold pass would
+  // (O = acc * (1 / l), rounded once at this write); otherwise it leaves its
+  // running state for the fold pass: acc in block slot 0, m and l in the LSE
+  // of block slots 0 and 1.
+  if (head && col < a.G) {
+    const int wave = threadIdx.x >> 6;
+    const int hq = hk * a.G + col;
+    const bool last = blk1 * BK >= len;
+    if (last) {
+      const Final fin = finalize(hf.st);
+      const int64_t row = (static_cast<int64_t>(seq) * a.Hq + hq) * kHeadDim;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d = wave * 32 + 8 * g + 4 * half;
+        const float o0 = hf.acc[4 * g] * fin.r, o1 = hf.acc[4 * g + 1] * fin.r;
+        const float o2 = hf.acc[4 * g + 2] * fin.r, o3 = hf.acc[4 * g + 3] * fin.r;
+        if constexpr (F32) {
+          *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + row + d) = f32x4{o0, o1, o2, o3};
+        } else {
+          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + row + d) = u32x2{pack_bf16(o0, o1), pack_bf16(o2, o3)};
+        }
+      }
+      if (wave == 0 && half == 0) a.lse[static_cast<int64_t>(seq) * a.Hq + hq] = fin.lse;
+    } else {
+      const int64_t item0 = static_cast<int64_t>(seq) * a.max_blocks * a.Hq + hq;  // block slot 0
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d = wave * 32 + 8 * g + 4 * half;
+        *reinterpret_cast<f32x4*>(a.items_out + item0 * kHeadDim + d) =
+            f32x4{hf.acc[4 * g], hf.acc[4 * g + 1], hf.acc[4 * g + 2], hf.acc[4 * g + 3]};
+      }
+      if (wave == 0 && half == 0) {
+        a.items_lse[item0] = hf.st.m;
+        a.items_lse[item0 + a.Hq] = hf.st.l;  // block slot 1
+      }
     }
   }
 }

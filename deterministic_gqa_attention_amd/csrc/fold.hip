@@ -4,8 +4,10 @@
 // One wave per (row, q head): lane l owns dims 2l and 2l+1.  The items are
 // folded with the scalar and element steps of core.hpp in the order given
 // (merge: the part order sorted by global block index on the host; decode:
-// ascending block index), then finalized and written (bf16 RNE or fp32) with
-// the natural-log LSE.  These are the same operations, in the same order, as
+// ascending block index, continuing from the running state the sequence's
+// head unit left after its blocks, or nothing at all when the head unit
+// covered the sequence and wrote the row itself), then finalized and written
+// (bf16 RNE or fp32) with the natural-log LSE.  These are the same operations, in the same order, as
 // the fold inside the fused prefill kernel, so a merge of per-block states
 // reproduces the fused result bit for bit.
 #include "kernels.hpp"
@@ -29,21 +31,35 @@ __global__ __launch_bounds__(kThreads) void fold_kernel(const FoldArgs a) {
   const int head = static_cast<int>(item % a.Hq);
 
   int n;
+  int start = 0;  // first item to fold
+  FoldState st{kNegInf, 0.0f};
+  float acc0 = 0.0f, acc1 = 0.0f;
   if constexpr (DECODE) {
     int64_t len = a.uniform_len;
     if (a.len_mode == kLensTable) len = a.lens[row];
     if (a.len_mode == kLensDevice) len = a.ctx_lens[row];
     len = len < 0 ? 0 : (len > a.len_cap ? a.len_cap : len);
     n = static_cast<int>((len + a.block - 1) / a.block);
+    // The sequence's head unit folded blocks [0, head_blocks) already: it
+    // wrote the final row itself when that was all of them, else its running
+    // state (acc in block slot 0, m and l in the LSE of slots 0 and 1).
+    if (n > 0 && n <= a.head_blocks) return;
+    if (n > a.head_blocks) {
+      const int64_t i0 = row * a.n_parts * a.Hq + head;
+      st.m = a.part_lse[i0];
+      st.l = a.part_lse[i0 + a.Hq];
+      const float2 x = *reinterpret_cast<const float2*>(a.part_out + i0 * kHeadDim + 2 * lane);
+      acc0 = x.x;
+      acc1 = x.y;
+      start = a.head_blocks;
+    }
   } else {
     n = a.n_parts;
   }
 
-  FoldState st{kNegInf, 0.0f};
-  float acc0 = 0.0f, acc1 = 0.0f;
   // Items are loaded kBatch at a time (all loads in flight together), then
   // folded one by one in order.
-  for (int i0 = 0; i0 < n; i0 += kBatch) {
+  for (int i0 = start; i0 < n; i0 += kBatch) {
     float L[kBatch];
     float2 o[kBatch];
 #pragma unroll

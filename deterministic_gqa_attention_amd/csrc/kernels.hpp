@@ -10,7 +10,8 @@ namespace rla {
 
 constexpr int kHeadDimPublic = 128;  // the only head dimension the kernels implement
 constexpr int kMaxParts = 512;  // partial states per merge / owned blocks per emit launch
-constexpr int kDecodeUnitBlocks = 4;  // KV blocks one decode workgroup walks
+constexpr int kDecodeUnitBlocks = 4;  // KV blocks of one decode tail unit
+constexpr int kDecodeIdsCap = 2048;   // page ids one decode workgroup stages (bounds its head unit)
 
 // Prefill and chunked prefill.  Query row t of batch b sits at absolute
 // position pos0 + t; it attends keys [0, kv_len) (and key <= position when
@@ -54,27 +55,35 @@ enum DecodeLenMode : int32_t {
   kLensTable = 2,    // lens[] / unit_start[] below; grid of exactly the units needed
 };
 
-// Paged decode, pass 1: one workgroup per (kv head, unit of up to
-// unit_blocks consecutive KV blocks of one sequence) writes each block's
-// partial state for the group's q heads.
+// Paged decode, pass 1: one workgroup per (kv head, unit of consecutive KV
+// blocks of one sequence).  Each sequence has one head unit, blocks
+// [0, min(nb, head_blocks)), which folds its blocks' partial states in
+// registers from the empty state and writes either the final output (the
+// head covers the sequence) or the running state; then tail units of up to
+// unit_blocks blocks each write every block's partial state for the group's
+// q heads.  The grid holds every head unit first (Bd per kv head), then the
+// tail units.
 struct DecodeArgs {
   const uint16_t* q;          // [Bd][Hq][D]
   const uint16_t* k_pool;     // [num_pages][Hkv][P][D]
   const uint16_t* v_pool;
   const int32_t* page_table;  // [Bd][max_pages]; null: page i of sequence s is s*max_pages + i
   const int32_t* ctx_lens;    // [Bd] (kLensDevice only)
-  float* items_out;           // [Bd][max_blocks][Hq][D]
-  float* items_lse;           // [Bd][max_blocks][Hq]
+  float* items_out;           // [Bd][max_blocks][Hq][D]; a head's running acc in block slot 0
+  float* items_lse;           // [Bd][max_blocks][Hq]; a head's running m, l in block slots 0, 1
+  void* out;                  // [Bd][Hq][D] bf16 or fp32: written by head units that cover their sequence
+  float* lse;                 // [Bd][Hq]
   int64_t num_pages;
   int32_t P, max_pages, Bd, Hq, Hkv, G, max_blocks, len_cap;
   int32_t log2_P;             // page size is a power of two (it divides the block)
-  int32_t unit_blocks;        // KV blocks per workgroup unit
+  int32_t unit_blocks;        // KV blocks per tail unit
+  int32_t head_blocks;        // KV blocks of a head unit (at most kDecodeIdsCap * P / block)
   int32_t len_mode;           // DecodeLenMode
-  int64_t n_units;            // units in the grid (per kv head)
+  int64_t n_units;            // units in the grid (per kv head): Bd heads, then the tails
   int32_t uniform_len;        // kLensUniform: context length of every sequence
   float c;
   int32_t lens[kDecodeTableSeqs];            // kLensTable: length of sequence s (validated, <= len_cap)
-  int32_t unit_start[kDecodeTableSeqs + 1];  // kLensTable: first unit of sequence s; [Bd] = n_units
+  int32_t unit_start[kDecodeTableSeqs + 1];  // kLensTable: first tail unit of sequence s; [Bd] = all tails
 };
 
 // Fold of per-block partial states in ascending block order (decode pass 2)
@@ -91,6 +100,7 @@ struct FoldArgs {
   int32_t Hq;
   int32_t n_parts;            // merge: parts to fold; decode: max_blocks
   int32_t block;              // decode: keys per block; merge: unused
+  int32_t head_blocks;        // decode: blocks folded by each sequence's head unit
   int32_t len_cap;            // decode: clamp on context lengths
   uint16_t order[kMaxParts];  // merge: part indices in fold order
   int32_t lens[kDecodeTableSeqs];  // decode, kLensTable: length of row s

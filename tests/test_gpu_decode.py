@@ -96,12 +96,17 @@ def test_decode_equals_prefill_last_row():
         assert_bitwise(dl[s], pl[0, L - 1], f"seq {s} LSE")
 
 
-# Lengths around the boundaries of the decode workgroup units (4 KV blocks:
-# 512 keys at 128-key blocks, 256 at 64): a sequence's last unit then holds
-# 1, 2, 3 or 4 blocks, with or without a block two ahead to prefetch.
-UNIT_LENS = np.array([255, 256, 257, 511, 512, 513, 640, 769, 1023, 1024, 1025, 1537, 2049, 2303], np.int32)
+# Lengths around the boundaries of the decode workgroup units.  A sequence's
+# head unit folds its first 64 blocks (8192 keys at 128-key blocks, 4096 at
+# 64) in registers; the rest goes to tail units of 4 blocks (512 / 256 keys),
+# whose last one then holds 1, 2, 3 or 4 blocks, with or without a block two
+# ahead to prefetch.  Short lengths end inside the head unit (odd and even
+# block counts, a lone block).
+UNIT_LENS = np.array([255, 256, 257, 511, 512, 513, 640, 769, 1023, 1024, 1025, 1537, 2049, 2303,
+                      4095, 4096, 4097, 4351, 4352, 4353, 4609,
+                      8191, 8192, 8193, 8703, 8704, 8705, 8833, 9217], np.int32)
 UNITS = gen.DecodeConfig(43, "decode unit boundaries", batch=len(UNIT_LENS), Hq=8, Hkv=2, D=128, page_size=16,
-                         num_pages=1024, len_lo=1, len_hi=2400, block=128)
+                         num_pages=8192, len_lo=1, len_hi=9300, block=128)
 
 
 @pytest.mark.parametrize("block", [64, 128])
@@ -118,6 +123,9 @@ def test_unit_boundaries_parity_and_prefill_identity(block):
                                  scale=cfg.softmax_scale)
     stats = check_parity(host_f64(do), host_f64(dl), ro, rl, f32_out=True, what="unit-boundary decode")
     say(f"    parity {stats}")
+    eo, el = _decode(d, cfg, block=block, out_dtype=torch.float32, host_lens=False)
+    assert_bitwise(eo, do, "Out with device lengths")
+    assert_bitwise(el, dl, "LSE with device lengths")
     P = cfg.page_size
     for s, L in enumerate(UNIT_LENS.tolist()):
         pages = d["page_table"][s, : -(-L // P)]

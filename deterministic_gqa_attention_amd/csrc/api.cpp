@@ -218,6 +218,9 @@ rla_status run_decode(const rla_attn_params* p, int g, const void* q, const void
       tails += tails_of(host_context_lens[i]);
     }
     d.unit_start[batch] = static_cast<int32_t>(tails);
+    for (int i = 0; i < batch; ++i) d.head_order[i] = static_cast<int16_t>(i);
+    std::stable_sort(d.head_order, d.head_order + batch,
+                     [&](int16_t x, int16_t y) { return host_context_lens[x] > host_context_lens[y]; });
     d.n_units = batch + tails;
   } else {
     // device lengths: every unit up to max_context_len, idle ones exit

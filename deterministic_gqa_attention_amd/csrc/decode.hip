@@ -44,7 +44,11 @@ struct DecodeLds {
   static constexpr int kMaxOff = kPOff + NKT * kPBytesPerTile;
   static constexpr int kSumOff = kMaxOff + NKT * 32 * 4;
   static constexpr int kPageOff = kSumOff + NKT * 32 * 4;
-  static constexpr int kBytes = kPageOff + kMaxUnitPages * 4;
+  // a tail unit's items: [block of the unit][head of the group][D] fp32, then
+  // the LSEs [block][head]
+  static constexpr int kStageOff = kPageOff + kMaxUnitPages * 4;
+  static constexpr int kStageLseOff = kStageOff + kDecodeUnitBlocks * kDecodeStageHeads * kHeadDim * 4;
+  static constexpr int kBytes = kStageLseOff + kDecodeUnitBlocks * kDecodeStageHeads * 4;
 };
 
 // The unit's slice of the page table, copied to LDS once so that the per-row
@@ -119,8 +123,9 @@ __device__ __forceinline__ int clamp_len(const DecodeArgs& a, int seq) {
 }
 
 // Map a unit index to (sequence, first block, end block, head or tail);
-// false for an idle unit.  Units [0, Bd) are the sequences' head units,
-// blocks [0, min(nb, head_blocks)); the rest are tail units of up to
+// false for an idle unit.  Units [0, Bd) are the sequences' head units
+// (kLensTable: in head_order), blocks [0, min(nb, head_blocks)); the rest are
+// tail units of up to
 // unit_blocks blocks from head_blocks on.  kLensTable: a tail's sequence is
 // the last one whose first tail unit (unit_start, a prefix sum the host built
 // from the lengths) is <= its index, found by a binary search over the launch
@@ -137,7 +142,7 @@ __device__ __forceinline__ bool locate_unit(const DecodeArgs& a, uint32_t u, int
   head = u < bd;
   uint32_t k = 0;  // tail index within the sequence
   if (head) {
-    seq = static_cast<int>(u);
+    seq = a.len_mode == kLensTable ? a.head_order[u] : static_cast<int>(u);
     len = a.len_mode == kLensTable ? a.lens[seq] : clamp_len(a, seq);
   } else {
     const uint32_t t = u - bd;
@@ -192,7 +197,8 @@ struct HeadFold {
 template <int BK, bool F32>
 __device__ __forceinline__ void decode_block(const DecodeArgs& a, char* lds, BlockRegs<BK>& br,
                                              const bf16x8 (&qf)[kDSteps], int seq, int hk, int blk, int len,
-                                             const UnitPages& up, int next_key0, bool head, HeadFold& hf) {
+                                             const UnitPages& up, int next_key0, bool head, HeadFold& hf,
+                                             int slot) {
   using Lay = DecodeLds<BK, F32>;
   constexpr int NKT = Lay::NKT;
   const char* lv = lds + Lay::kVOff;  // V rows at lv + TileLayout::v_rel(...)
@@ -286,6 +292,19 @@ __device__ __forceinline__ void decode_block(const DecodeArgs& a, char* lds, Blo
     const FoldStep f = fold_scalars(hf.st, sc.L);
 #pragma unroll
     for (int i = 0; i < 16; ++i) hf.acc[i] = fold_elem(f, hf.acc[i], item_out(acc[i], sc));
+  } else if (a.G <= kDecodeStageHeads) {
+    // tail unit: the items wait in LDS for the unit's end (see flush_items)
+    if (col < a.G) {
+      float* so = reinterpret_cast<float*>(lds + Lay::kStageOff) + (slot * kDecodeStageHeads + col) * kHeadDim;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d = dt * 32 + 8 * g + 4 * half;
+        *reinterpret_cast<f32x4*>(so + d) = f32x4{item_out(acc[4 * g], sc), item_out(acc[4 * g + 1], sc),
+                                                  item_out(acc[4 * g + 2], sc), item_out(acc[4 * g + 3], sc)};
+      }
+      if (wave == 0 && half == 0)
+        reinterpret_cast<float*>(lds + Lay::kStageLseOff)[slot * kDecodeStageHeads + col] = sc.L;
+    }
   } else if (col < a.G) {
     const int head = hk * a.G + col;
     const int64_t item = (static_cast<int64_t>(seq) * a.max_blocks + blk) * a.Hq + head;
@@ -362,15 +381,40 @@ __global__ __launch_bounds__(kThreads, 2) void decode_items_kernel(const DecodeA
     r0.store_v(lv);
     if (n0 >= 0) r0.load_v(a, up, hk, n0, len);
     lds_barrier();  // V of blk visible
-    decode_block<BK, F32>(a, lds, r0, qf, seq, hk, blk, len, up, n0, head, hf);
+    decode_block<BK, F32>(a, lds, r0, qf, seq, hk, blk, len, up, n0, head, hf, blk - blk0);
     lds_barrier();  // everyone done with V / P of blk
     if (blk + 1 < blk1) {
       const int n1 = blk + 3 < blk1 ? (blk + 3) * BK : -1;
       r1.store_v(lv);
       if (n1 >= 0) r1.load_v(a, up, hk, n1, len);
       lds_barrier();
-      decode_block<BK, F32>(a, lds, r1, qf, seq, hk, blk + 1, len, up, n1, head, hf);
+      decode_block<BK, F32>(a, lds, r1, qf, seq, hk, blk + 1, len, up, n1, head, hf, blk + 1 - blk0);
       lds_barrier();
+    }
+  }
+
+  // A tail unit writes its items now, after its last wait for KV loads: item
+  // stores count in the same in-order counter as the loads, so a store issued
+  // between blocks would make the next block's wait for its KV data also wait
+  // for the store's completion, which under the full read stream is slow.
+  // (The loop's last barrier made the staged items visible.)
+  if (!head && a.G <= kDecodeStageHeads) {
+    const int per = a.G * (kHeadDim / 4);  // 16-byte chunks of one block's items
+    const int n = (blk1 - blk0) * per;
+    const char* so = lds + Lay::kStageOff;
+    for (int c = threadIdx.x; c < n; c += kThreads) {
+      const int j = c / per;
+      const int r = c - j * per;
+      const int64_t item0 = (static_cast<int64_t>(seq) * a.max_blocks + blk0 + j) * a.Hq + hk * a.G;
+      *reinterpret_cast<f32x4*>(a.items_out + item0 * kHeadDim + 4 * r) =
+          *reinterpret_cast<const f32x4*>(so + (j * kDecodeStageHeads * kHeadDim + 4 * r) * 4);
+    }
+    const float* sl = reinterpret_cast<const float*>(lds + Lay::kStageLseOff);
+    for (int c = threadIdx.x; c < (blk1 - blk0) * a.G; c += kThreads) {
+      const int j = c / a.G;
+      const int h = c - j * a.G;
+      a.items_lse[(static_cast<int64_t>(seq) * a.max_blocks + blk0 + j) * a.Hq + hk * a.G + h] =
+          sl[j * kDecodeStageHeads + h];
     }
   }
 

@@ -12,6 +12,7 @@ constexpr int kHeadDimPublic = 128;  // the only head dimension the kernels impl
 constexpr int kMaxParts = 512;  // partial states per merge / owned blocks per emit launch
 constexpr int kDecodeUnitBlocks = 4;  // KV blocks of one decode tail unit
 constexpr int kDecodeIdsCap = 2048;   // page ids one decode workgroup stages (bounds its head unit)
+constexpr int kDecodeStageHeads = 8;  // groups of up to this many q heads stage a tail's items in LDS
 
 // Prefill and chunked prefill.  Query row t of batch b sits at absolute
 // position pos0 + t; it attends keys [0, kv_len) (and key <= position when
@@ -61,8 +62,9 @@ enum DecodeLenMode : int32_t {
 // registers from the empty state and writes either the final output (the
 // head covers the sequence) or the running state; then tail units of up to
 // unit_blocks blocks each write every block's partial state for the group's
-// q heads.  The grid holds every head unit first (Bd per kv head), then the
-// tail units.
+// q heads.  The grid holds every head unit first (Bd per kv head; with the
+// length table, longest sequence first, so the long heads start together and
+// the short ones leave room for tails early), then the tail units.
 struct DecodeArgs {
   const uint16_t* q;          // [Bd][Hq][D]
   const uint16_t* k_pool;     // [num_pages][Hkv][P][D]
@@ -84,6 +86,7 @@ struct DecodeArgs {
   float c;
   int32_t lens[kDecodeTableSeqs];            // kLensTable: length of sequence s (validated, <= len_cap)
   int32_t unit_start[kDecodeTableSeqs + 1];  // kLensTable: first tail unit of sequence s; [Bd] = all tails
+  int16_t head_order[kDecodeTableSeqs];     // kLensTable: sequence of head unit u (longest first)
 };
 
 // Fold of per-block partial states in ascending block order (decode pass 2)

@@ -203,6 +203,32 @@ __device__ __forceinline__ FoldStep fold_scalars(FoldState& st, float L) {
   return f;
 }
 
+// The same step with every case computed as a select instead of a branch:
+// the one exponential takes (m - L) for a move and (L - m) otherwise, and the
+// cases pick their results from it, so the values are those of fold_scalars
+// bit for bit.  Sequential folds of many items (the fold pass, a decode head
+// unit) spend most of their time on this dependent chain, which branches
+// lengthen.
+__device__ __forceinline__ FoldStep fold_scalars_sel(FoldState& st, float L) {
+  const bool empty = L == kNegInf;
+  const bool first = !empty && st.m == kNegInf;
+  const bool mv = !empty && !first && L > st.m + kFoldTau;
+  const bool add = !empty && !first && !mv;
+  const float x = mv ? st.m : L;
+  const float y = mv ? L : st.m;
+  const float e = fold_exp(x - y);  // unused (and possibly not finite) for empty and first
+  const float la = st.l * e;
+  FoldStep f;
+  f.move = mv;
+  f.alpha = mv ? e : 1.0f;
+  f.beta = empty ? 0.0f : (add ? e : 1.0f);
+  const float l_add = st.l + e;
+  const float l_move = la + 1.0f;
+  st.l = first ? 1.0f : (mv ? l_move : (add ? l_add : st.l));
+  st.m = (first || mv) ? L : st.m;
+  return f;
+}
+
 // Element part of one fold step.
 __device__ __forceinline__ float fold_elem(const FoldStep& f, float acc, float o) {
   return fmaf(o, f.beta, acc * f.alpha);

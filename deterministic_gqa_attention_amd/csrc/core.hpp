@@ -179,37 +179,12 @@ struct FoldStep {
   bool move;
 };
 
-// Scalar part of one fold step (updates m and l).
+// Scalar part of one fold step (updates m and l), with every case computed
+// as a select rather than a branch: the one exponential takes (m - L) for a
+// move and (L - m) otherwise, and each case picks its results from it.  The
+// step sits on the dependent chain of every sequential fold (the fused
+// prefill kernel, a decode head unit, the fold pass), which branches lengthen.
 __device__ __forceinline__ FoldStep fold_scalars(FoldState& st, float L) {
-  FoldStep f;
-  f.alpha = 1.0f;
-  f.beta = 1.0f;
-  f.move = false;
-  if (L == kNegInf) {
-    f.beta = 0.0f;
-  } else if (st.m == kNegInf) {
-    st.m = L;
-    st.l = 1.0f;
-  } else if (L > st.m + kFoldTau) {
-    f.move = true;
-    f.alpha = fold_exp(st.m - L);
-    const float la = st.l * f.alpha;
-    st.l = la + 1.0f;
-    st.m = L;
-  } else {
-    f.beta = fold_exp(L - st.m);
-    st.l = st.l + f.beta;
-  }
-  return f;
-}
-
-// The same step with every case computed as a select instead of a branch:
-// the one exponential takes (m - L) for a move and (L - m) otherwise, and the
-// cases pick their results from it, so the values are those of fold_scalars
-// bit for bit.  Sequential folds of many items (the fold pass, a decode head
-// unit) spend most of their time on this dependent chain, which branches
-// lengthen.
-__device__ __forceinline__ FoldStep fold_scalars_sel(FoldState& st, float L) {
   const bool empty = L == kNegInf;
   const bool first = !empty && st.m == kNegInf;
   const bool mv = !empty && !first && L > st.m + kFoldTau;
@@ -220,10 +195,10 @@ __device__ __forceinline__ FoldStep fold_scalars_sel(FoldState& st, float L) {
   const float la = st.l * e;
   FoldStep f;
   f.move = mv;
-  f.alpha = mv ? e : 1.0f;
-  f.beta = empty ? 0.0f : (add ? e : 1.0f);
-  const float l_add = st.l + e;
-  const float l_move = la + 1.0f;
+  f.alpha = mv ? e : 1.0f;                            // move: e^(m - L)
+  f.beta = empty ? 0.0f : (add ? e : 1.0f);           // add: e^(L - m)
+  const float l_add = st.l + e;                       // add: l + beta
+  const float l_move = la + 1.0f;                     // move: l * alpha + 1
   st.l = first ? 1.0f : (mv ? l_move : (add ? l_add : st.l));
   st.m = (first || mv) ? L : st.m;
   return f;

@@ -289,7 +289,7 @@ __device__ __forceinline__ void decode_block(const DecodeArgs& a, char* lds, Blo
   }
   const ItemScalars sc = item_scalars(m_t, l_b);
   if (head) {
-    const FoldStep f = fold_scalars_sel(hf.st, sc.L);
+    const FoldStep f = fold_scalars(hf.st, sc.L);
 #pragma unroll
     for (int i = 0; i < 16; ++i) hf.acc[i] = fold_elem(f, hf.acc[i], item_out(acc[i], sc));
   } else if (a.G <= kDecodeStageHeads) {

@@ -81,7 +81,7 @@ __global__ __launch_bounds__(kThreads) void fold_kernel(const FoldArgs a) {
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
       if (i0 + j < n) {
-        const FoldStep f = fold_scalars_sel(st, L[j]);
+        const FoldStep f = fold_scalars(st, L[j]);
         acc0 = fold_elem(f, acc0, o[j].x);
         acc1 = fold_elem(f, acc1, o[j].y);
       }

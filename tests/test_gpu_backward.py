@@ -1,13 +1,18 @@
 """GPU backward (dQ, dK, dV) against the FP64 oracle, and its bitwise
 invariances, through the C ABI.
 
-Parity bar.  The kernels round P and dS to bf16 as MFMA operands and take
-Delta from the bf16 forward output, so an element's error is bounded by a
-small multiple of the sums of absolute values that the oracle reports with
-the gradient (mag_*: the terms of the element's sum, each widened by the parts
-of dS an error in Delta or dP can move).  bf16 rounding contributes at most
-2^-8 relative per term, the Delta and dP errors less than that relative to
-their magnitudes; the test requires |gpu - oracle| <= 2^-6 * mag.
+Parity bar.  The oracle reports with each gradient element mag, the sum of
+the absolute values of its terms, each widened by the part of dS an error in
+Delta can move (p * sum_j p_j |dP_j|).  Each term carries at most one bf16
+rounding in the kernels (unit roundoff 2^-8): P as the dV operand, scale*dS as
+the dQ and dK operand.  Delta comes from the bf16 forward output, whose
+rounding moves it by at most 2^-8 * sum_d |dOut_d||Out_d| <= 2^-8 *
+sum_j p_j |dP_j|, inside the widening.  FP32 accumulation adds at most about
+n * 2^-24 relative over n <= 2^14 terms (2^-10).  So |gpu - oracle| <=
+(2^-8 + 2^-10) * mag, and the test requires 2^-7 * mag.  tests/test_grad_bar.py
+shows on the CPU that a model of these roundings stays well inside this bar
+while plausible mistakes (Delta from the wrong row, a dropped scale, ...)
+exceed it several times over.
 """
 import numpy as np
 import pytest
@@ -20,7 +25,7 @@ from tests.gpu_util import assert_bitwise, dev_bf16, host_f64, say
 
 pytestmark = pytest.mark.gpu
 
-GRAD_FACTOR = 2.0 ** -6
+GRAD_FACTOR = 2.0 ** -7
 GRAD_FLOOR = 1e-12
 
 
@@ -50,7 +55,7 @@ def _check(got, ref, mag, what):
     bound = GRAD_FACTOR * mag + GRAD_FLOOR
     bad = err > bound
     ratio = float((err / np.maximum(bound, 1e-30)).max(initial=0.0))
-    assert not bad.any(), (f"{what}: {int(bad.sum())} elements exceed 2^-6 * mag; max abs err "
+    assert not bad.any(), (f"{what}: {int(bad.sum())} elements exceed 2^-7 * mag; max abs err "
                            f"{err.max():.3e}, worst err/bound {ratio:.3f}")
     return float(err.max(initial=0.0)), ratio
 

@@ -634,12 +634,12 @@ __global__ __launch_bounds__(kThreads) void prefill_pp_kernel(const PrefillArgs 
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
 
-  // Loads of half-step 2i (group 1): K_{i+1} into the K array of parity
-  // (i+1)&1 and V_i into the V array of parity i&1.  par = i & 1.
-  // fragment addresses of buffer 0 of each pair, computed once; buffer 1 of a
-  // pair sits at a fixed distance, so every read is one register + immediate
+  // Fragment addresses of buffer 0 of each pair, computed once; buffer 1 of a
+  // pair sits at a fixed distance, so every read is one register + immediate.
   const KReads<BK> kr0(kb0, opaque_lane());
   const VReads<BK> vr0(vb0, opaque_lane());
+  // Loads of half-step 2i (group 1): K_{i+1} into the K array of parity
+  // (i+1)&1 and V_i into the V array of parity i&1.  par = i & 1.
   auto loads = [&](auto par, int i) {
     constexpr int p = decltype(par)::value;
     if (i + 1 < nblk) ld.issue_k(p ? kb0 : kb1, w.krs, (i + 1) * BK);

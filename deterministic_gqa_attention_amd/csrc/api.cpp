@@ -193,10 +193,18 @@ rla_status run_decode(const rla_attn_params* p, int g, const void* q, const void
   d.len_cap = static_cast<int32_t>(cap);
   d.c = score_scale(p);
   d.unit_blocks = rla::kDecodeUnitBlocks;
-  // Head units fold up to 64 blocks each (fewer where the unit's page ids
-  // would not fit the workgroup's staging area: small pages).
-  d.head_blocks = static_cast<int32_t>(std::min<int64_t>(
-      64, static_cast<int64_t>(rla::kDecodeIdsCap) * page_size / p->kv_block_size));
+  // Head units fold up to 64 blocks each.  That saves those blocks' item
+  // writes, but one workgroup walks them in turn, so heads are that long only
+  // when the head units alone fill the GPU's decode workgroup slots (256 CUs,
+  // two each); with fewer (sequence, kv head) pairs they shrink in proportion,
+  // down to one tail unit's length, keeping a small batch spread over many
+  // workgroups.  Their page ids must also fit the workgroup's staging area.
+  constexpr int64_t kSlots = 512;
+  const int64_t pairs = static_cast<int64_t>(batch) * p->num_kv_heads;
+  int64_t head = pairs >= kSlots ? 64 : 64 * pairs / kSlots / rla::kDecodeUnitBlocks * rla::kDecodeUnitBlocks;
+  head = std::max<int64_t>(head, rla::kDecodeUnitBlocks);
+  head = std::min<int64_t>(head, static_cast<int64_t>(rla::kDecodeIdsCap) * page_size / p->kv_block_size);
+  d.head_blocks = static_cast<int32_t>(head);
   d.out = out;
   d.lse = lse;
   auto tails_of = [&](int64_t len) {

@@ -97,15 +97,19 @@ def test_decode_equals_prefill_last_row():
 
 
 # Lengths around the boundaries of the decode workgroup units.  A sequence's
-# head unit folds its first 64 blocks (8192 keys at 128-key blocks, 4096 at
-# 64) in registers; the rest goes to tail units of 4 blocks (512 / 256 keys),
-# whose last one then holds 1, 2, 3 or 4 blocks, with or without a block two
-# ahead to prefetch.  Short lengths end inside the head unit (odd and even
-# block counts, a lone block).
+# head unit folds its first blocks in registers: 64 of them (8192 keys at
+# 128-key blocks, 4096 at 64) when the batch has at least 512 (sequence, kv
+# head) pairs, fewer for smaller batches, down to 4.  The rest goes to tail
+# units of 4 blocks (512 / 256 keys), whose last one then holds 1, 2, 3 or 4
+# blocks, with or without a block two ahead to prefetch.  Short lengths end
+# inside the head unit (odd and even block counts, a lone block).  The batch
+# is padded with one-key sequences to 256 sequences x 2 kv heads = 512 pairs,
+# so its heads are 64 blocks long; the same sequences alone get 4-block heads.
 UNIT_LENS = np.array([255, 256, 257, 511, 512, 513, 640, 769, 1023, 1024, 1025, 1537, 2049, 2303,
                       4095, 4096, 4097, 4351, 4352, 4353, 4609,
                       8191, 8192, 8193, 8703, 8704, 8705, 8833, 9217], np.int32)
-UNITS = gen.DecodeConfig(43, "decode unit boundaries", batch=len(UNIT_LENS), Hq=8, Hkv=2, D=128, page_size=16,
+UNIT_BATCH = np.concatenate([UNIT_LENS, np.ones(256 - UNIT_LENS.size, np.int32)])
+UNITS = gen.DecodeConfig(43, "decode unit boundaries", batch=UNIT_BATCH.size, Hq=8, Hkv=2, D=128, page_size=16,
                          num_pages=8192, len_lo=1, len_hi=9300, block=128)
 
 
@@ -115,7 +119,7 @@ def test_unit_boundaries_parity_and_prefill_identity(block):
     every sequence's Out/LSE equal the last row of a causal prefill over the
     same tokens, bitwise."""
     cfg = dataclasses.replace(UNITS, block=block)
-    d = gen.decode_inputs(cfg, lengths=UNIT_LENS)
+    d = gen.decode_inputs(cfg, lengths=UNIT_BATCH)
     say(f"[decode] unit boundaries block={block}")
     do, dl = _decode(d, cfg, block=block, out_dtype=torch.float32)
     torch.cuda.synchronize()
@@ -126,6 +130,11 @@ def test_unit_boundaries_parity_and_prefill_identity(block):
     eo, el = _decode(d, cfg, block=block, out_dtype=torch.float32, host_lens=False)
     assert_bitwise(eo, do, "Out with device lengths")
     assert_bitwise(el, dl, "LSE with device lengths")
+    # the boundary sequences alone: 58 pairs, so 4-block heads and all else in tails
+    n = UNIT_LENS.size
+    so, sl = _decode(d, cfg, block=block, out_dtype=torch.float32, seqs=np.arange(n))
+    assert_bitwise(so, do[:n], "Out with short heads")
+    assert_bitwise(sl, dl[:n], "LSE with short heads")
     P = cfg.page_size
     for s, L in enumerate(UNIT_LENS.tolist()):
         pages = d["page_table"][s, : -(-L // P)]

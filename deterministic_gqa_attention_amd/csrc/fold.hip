@@ -23,7 +23,10 @@ constexpr int kBatch = 32;  // items in flight per wave
 
 template <bool DECODE, bool F32>
 __global__ __launch_bounds__(kThreads) void fold_kernel(const FoldArgs a) {
-  const int wave = threadIdx.x >> 6;
+  // wave index made provably uniform: the row, its item count and every
+  // per-item condition below are then scalar, and the conditions scalar
+  // branches
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
   const int lane = threadIdx.x & 63;
   const int64_t item = static_cast<int64_t>(blockIdx.x) * kWaves + wave;  // row * Hq + head
   if (item >= a.rows * a.Hq) return;
@@ -39,7 +42,7 @@ __global__ __launch_bounds__(kThreads) void fold_kernel(const FoldArgs a) {
     if (a.len_mode == kLensTable) len = a.lens[row];
     if (a.len_mode == kLensDevice) len = a.ctx_lens[row];
     len = len < 0 ? 0 : (len > a.len_cap ? a.len_cap : len);
-    n = static_cast<int>((len + a.block - 1) / a.block);
+    n = __builtin_amdgcn_readfirstlane(static_cast<int>((len + a.block - 1) / a.block));  // one row per wave
     // The sequence's head unit folded blocks [0, head_blocks) already: it
     // wrote the final row itself when that was all of them, else its running
     // state (acc in block slot 0, m and l in the LSE of slots 0 and 1).

@@ -59,6 +59,7 @@ rla_status check_params(const rla_attn_params* p, bool attention_call, int* grou
   if (p->num_q_heads % p->num_kv_heads != 0)
     return fail(RLA_ERR_BAD_SHAPE, "Hq=%d is not a multiple of Hkv=%d", p->num_q_heads, p->num_kv_heads);
   const int g = p->num_q_heads / p->num_kv_heads;
+  static_assert(rla::kDecodeStageHeads >= 8, "decode tail units stage the items of groups of up to 8 q heads");
   if (g != 1 && g != 2 && g != 4 && g != 8)
     return fail(RLA_ERR_UNSUPPORTED, "GQA group Hq/Hkv=%d not in {1,2,4,8}", g);
   if (p->kv_block_size != 64 && p->kv_block_size != 128)

@@ -292,30 +292,18 @@ __device__ __forceinline__ void decode_block(const DecodeArgs& a, char* lds, Blo
     const FoldStep f = fold_scalars(hf.st, sc.L);
 #pragma unroll
     for (int i = 0; i < 16; ++i) hf.acc[i] = fold_elem(f, hf.acc[i], item_out(acc[i], sc));
-  } else if (a.G <= kDecodeStageHeads) {
-    // tail unit: the items wait in LDS for the unit's end (see flush_items)
-    if (col < a.G) {
-      float* so = reinterpret_cast<float*>(lds + Lay::kStageOff) + (slot * kDecodeStageHeads + col) * kHeadDim;
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d = dt * 32 + 8 * g + 4 * half;
-        *reinterpret_cast<f32x4*>(so + d) = f32x4{item_out(acc[4 * g], sc), item_out(acc[4 * g + 1], sc),
-                                                  item_out(acc[4 * g + 2], sc), item_out(acc[4 * g + 3], sc)};
-      }
-      if (wave == 0 && half == 0)
-        reinterpret_cast<float*>(lds + Lay::kStageLseOff)[slot * kDecodeStageHeads + col] = sc.L;
-    }
   } else if (col < a.G) {
-    const int head = hk * a.G + col;
-    const int64_t item = (static_cast<int64_t>(seq) * a.max_blocks + blk) * a.Hq + head;
-    float* po = a.items_out + item * kHeadDim;
+    // tail unit: the items wait in LDS for the unit's end (written after the
+    // block loop)
+    float* so = reinterpret_cast<float*>(lds + Lay::kStageOff) + (slot * kDecodeStageHeads + col) * kHeadDim;
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int d = dt * 32 + 8 * g + 4 * half;
-      *reinterpret_cast<f32x4*>(po + d) = f32x4{item_out(acc[4 * g], sc), item_out(acc[4 * g + 1], sc),
+      *reinterpret_cast<f32x4*>(so + d) = f32x4{item_out(acc[4 * g], sc), item_out(acc[4 * g + 1], sc),
                                                 item_out(acc[4 * g + 2], sc), item_out(acc[4 * g + 3], sc)};
     }
-    if (wave == 0 && half == 0) a.items_lse[item] = sc.L;
+    float* sl = reinterpret_cast<float*>(lds + Lay::kStageLseOff);
+    if (wave == 0 && half == 0) sl[slot * kDecodeStageHeads + col] = sc.L;
   }
   if constexpr (F32) {
     if (next_key0 >= 0) br.load_k(a, up, hk, next_key0, len);
@@ -398,7 +386,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_items_kernel(const DecodeA
   // between blocks would make the next block's wait for its KV data also wait
   // for the store's completion, which under the full read stream is slow.
   // (The loop's last barrier made the staged items visible.)
-  if (!head && a.G <= kDecodeStageHeads) {
+  if (!head) {
     const int per = a.G * (kHeadDim / 4);  // 16-byte chunks of one block's items
     const int n = (blk1 - blk0) * per;
     const char* so = lds + Lay::kStageOff;

@@ -12,7 +12,7 @@ constexpr int kHeadDimPublic = 128;  // the only head dimension the kernels impl
 constexpr int kMaxParts = 512;  // partial states per merge / owned blocks per emit launch
 constexpr int kDecodeUnitBlocks = 4;  // KV blocks of one decode tail unit
 constexpr int kDecodeIdsCap = 2048;   // page ids one decode workgroup stages (bounds its head unit)
-constexpr int kDecodeStageHeads = 8;  // groups of up to this many q heads stage a tail's items in LDS
+constexpr int kDecodeStageHeads = 8;  // q heads per group a tail unit stages in LDS (the largest group accepted)
 
 // Prefill and chunked prefill.  Query row t of batch b sits at absolute
 // position pos0 + t; it attends keys [0, kv_len) (and key <= position when

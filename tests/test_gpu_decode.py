@@ -240,3 +240,31 @@ def test_more_sequences_than_the_launch_table():
         o, l = _decode(d, cfg, block=128, seqs=seqs)
         assert_bitwise(o, big_o[seqs[0]:seqs[-1] + 1], f"Out of sequences {seqs[0]}..{seqs[-1]}")
         assert_bitwise(l, big_l[seqs[0]:seqs[-1] + 1], f"LSE of sequences {seqs[0]}..{seqs[-1]}")
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(8, 8), (8, 4), (16, 2)], ids=["G1", "G2", "G8"])
+def test_group_sizes_parity_and_prefill_identity(Hq, Hkv):
+    """GQA groups of 1, 2 and 8 q heads per kv head (the decode kernel's MFMA
+    columns, staged tail items and head-unit fold per q head): parity with the
+    oracle and the last prefill row, bitwise, on lengths that end in the head
+    unit, in a full tail unit and in a partial one."""
+    lens = np.array([1, 200, 640, 1100, 1537], np.int32)
+    cfg = gen.DecodeConfig(48, "decode group sizes", batch=lens.size, Hq=Hq, Hkv=Hkv, D=128, page_size=16,
+                           num_pages=512, len_lo=1, len_hi=1600, block=128)
+    d = gen.decode_inputs(cfg, lengths=lens)
+    say(f"[decode] group size {Hq // Hkv}")
+    do, dl = _decode(d, cfg, block=128, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ro, rl = oracle.decode_paged(d["q"], d["k_pool"], d["v_pool"], d["page_table"], d["ctx_lens"],
+                                 scale=cfg.softmax_scale)
+    check_parity(host_f64(do), host_f64(dl), ro, rl, f32_out=True, what=f"decode G={Hq // Hkv}")
+    P = cfg.page_size
+    for s, L in enumerate(lens.tolist()):
+        pages = d["page_table"][s, : -(-L // P)]
+        k = d["k_pool"][pages].transpose(0, 2, 1, 3).reshape(-1, Hkv, 128)[:L][None]
+        v = d["v_pool"][pages].transpose(0, 2, 1, 3).reshape(-1, Hkv, 128)[:L][None]
+        q = np.zeros((1, L, Hq, 128), np.uint16)
+        q[0, L - 1] = d["q"][s]
+        po, pl = api.prefill(dev_bf16(q), dev_bf16(k), dev_bf16(v), block=128, out_dtype=torch.float32)
+        assert_bitwise(do[s], po[0, L - 1], f"G={Hq // Hkv} len {L} Out")
+        assert_bitwise(dl[s], pl[0, L - 1], f"G={Hq // Hkv} len {L} LSE")

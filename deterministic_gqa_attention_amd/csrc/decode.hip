@@ -1,20 +1,20 @@
 // Paged-KV decode, pass 1 (gfx950): one workgroup per (kv head, unit of
 // consecutive KV blocks of one sequence) computes each block's partial state
-// for the q heads of the group.  A sequence's head unit (its first 64 blocks
-// or fewer) folds those states in registers, in block order from the empty
-// state, with the fold pass's own steps, and writes the finished row (when it
-// covers the sequence) or its running state; the tail units write every
-// block's state to the caller's workspace, and pass 2 (fold.hip) continues the
-// fold from the head's state over them in ascending block index.  Folding in
-// the head unit saves most of the item writes (which cost far more than their
-// share of the bytes) and most of the per-workgroup set-up.  The cut into
-// units is fixed by the lengths alone and never changes what any block's state
-// holds or the order it is folded in.  Decode is bound by reading the KV
-// cache, so each workgroup keeps two
-// register sets of blocks (K as MFMA A-fragments, V rows bound for LDS) and
-// refills a set with the block two ahead as soon as its registers are free:
-// V right after it is staged in LDS, K right after the score MFMAs have read
-// it.  Two workgroups share a CU.
+// for the q heads of the group.  A sequence's head unit (its first blocks, up
+// to 64 of them) folds those states in registers, in block order from the
+// empty state, with the fold pass's own steps, and writes the finished row
+// (when it covers the sequence) or its running state; the tail units write
+// every block's state to the caller's workspace, and pass 2 (fold.hip)
+// continues the fold from the head's state over them in ascending block
+// index.  Folding in the head unit saves most of the item writes (which cost
+// far more than their share of the bytes) and most of the per-workgroup
+// set-up.  The cut into units is fixed by the lengths alone and never changes
+// what any block's state holds or the order it is folded in.  Decode is bound
+// by reading the KV cache, so each workgroup keeps two register sets of blocks
+// (K as MFMA A-fragments, V rows bound for LDS) and refills a set with the
+// block two ahead as soon as its registers are free: V right after it is
+// staged in LDS, K right after the score MFMAs have read it.  Two workgroups
+// share a CU.
 //
 // Keys are gathered through the page table: key j of sequence s is slot j % P
 // of page page_table[s][j / P] in a pool laid out [page][kv head][slot][dim].
@@ -65,7 +65,7 @@ struct UnitPages {
 __device__ __forceinline__ int64_t page_row_off(const DecodeArgs& a, const UnitPages& up, int hk, int key) {
   int page = up.ids[(key >> a.log2_P) - up.first];
   page = page < 0 ? 0 : (page >= a.num_pages ? static_cast<int>(a.num_pages - 1) : page);
-  const int64_t row = (static_cast<int64_t>(page * a.Hkv + hk) << a.log2_P) + (key & ((1 << a.log2_P) - 1));
+  const int64_t row = ((static_cast<int64_t>(page) * a.Hkv + hk) << a.log2_P) + (key & ((1 << a.log2_P) - 1));
   return row * kHeadDim;
 }
 

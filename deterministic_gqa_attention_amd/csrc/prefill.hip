@@ -15,18 +15,15 @@
 //   pv       acc_b = V^T P^T per dim tile     (matrix cores, V from LDS)
 //   fold     O_b = acc_b / l_b into the running state (vector ALU)
 // with the operations of core.hpp.  The bf16-output kernel
-// (prefill_pp_kernel) runs the two halves of the workgroup one stage apart
-// (ping-pong), so on every SIMD a scores stage (matrix cores) overlaps a
-// softmax + PV + fold stage (vector ALU) of the other wave; its paged variant
-// (prefill_pipe_kernel) is software pipelined over blocks instead: a scores
-// stage for block j, then a vector stage that runs the softmax of block j
-// slot by slot with the PV MFMAs and the fold of block j-1, each stage ended
-// by a workgroup barrier.  The fp32-output kernel runs scores | softmax |
-// pv+fold one after the other.  K/V blocks arrive by direct buffer->LDS loads; the per-block
-// step takes the buffer being read and the buffer being filled as restrict
-// pointers, so the compiler knows they do not overlap and never stalls an
-// LDS read on the in-flight loads (it would otherwise wait for every
-// outstanding direct load before the first read).  No atomics and no split
+// (prefill_pp_kernel, contiguous and paged caches) runs the two halves of
+// the workgroup one stage apart (ping-pong), so on every SIMD a scores stage
+// (matrix cores) overlaps a softmax + PV + fold stage (vector ALU) of the
+// other wave.  The fp32-output kernel runs scores | softmax | pv+fold one
+// after the other.  K/V blocks arrive by direct buffer->LDS loads; each
+// kernel names the buffer being read and the buffer being filled as separate
+// arrays (or restrict pointers), so the compiler knows they do not overlap
+// and never stalls an LDS read on the in-flight loads (it would otherwise
+// wait for every outstanding direct load before the first read).  No atomics and no split
 // of a block across workgroups, so nothing depends on scheduling.
 #include <type_traits>
 
@@ -84,32 +81,6 @@ __device__ __forceinline__ void block_scores_kr(const KReads<BK>& kr, const bf16
     const int ds = i % kDSteps;
     if (i + R - 1 < N) kf[(i + R - 1) % R] = kr.frag((i + R - 1) / kDSteps, (i + R - 1) % kDSteps);
     s[kt] = mfma(kf[i % R], qf[ds], ds == 0 ? f32x16{} : s[kt]);
-    sched_fence();
-  }
-}
-
-// The same with the Q B-fragments read from LDS: step ds of this lane at
-// qlane + ds*1024 (the wave's 8 KiB Q tile stored in fragment order).
-template <int BK>
-__device__ __forceinline__ void block_scores_q(const char* kreg, const char* qlane, f32x16 (&s)[BK / 32]) {
-  constexpr int NKT = BK / 32;
-  const KReads<BK> kr(kreg);
-#pragma unroll
-  for (int kt = 0; kt < NKT; ++kt) s[kt] = f32x16{};
-  bf16x8 kf[2][NKT];
-  bf16x8 qf[2];
-#pragma unroll
-  for (int kt = 0; kt < NKT; ++kt) kf[0][kt] = kr.frag(kt, 0);
-  qf[0] = as_bf16x8(*reinterpret_cast<const u32x4*>(qlane));
-#pragma unroll
-  for (int ds = 0; ds < kDSteps; ++ds) {
-    if (ds + 1 < kDSteps) {
-#pragma unroll
-      for (int kt = 0; kt < NKT; ++kt) kf[(ds + 1) & 1][kt] = kr.frag(kt, ds + 1);
-      qf[(ds + 1) & 1] = as_bf16x8(*reinterpret_cast<const u32x4*>(qlane + (ds + 1) * 1024));
-    }
-#pragma unroll
-    for (int kt = 0; kt < NKT; ++kt) s[kt] = mfma(kf[ds & 1][kt], qf[ds & 1], s[kt]);
     sched_fence();
   }
 }
@@ -273,67 +244,6 @@ __device__ __forceinline__ void block_pv_fold(const VReads<BK>& vr, const BlockP
   fold_tile(acc[3], ab1, in);
 }
 
-// The vector stage of the software-pipelined kernel: the softmax of block j
-// (scores s, already masked) runs on the vector ALU while the matrix cores
-// run the PV MFMAs of block j-1, dim tile by dim tile; each tile is folded
-// into the running state as soon as its MFMA chain ends.  The work is cut
-// into slots of one PV MFMA each; a slot also computes two softmax elements
-// (p, their bf16 pair and the canonical sum tree as its operands complete),
-// and slots are fenced so the scheduler cannot bunch the MFMAs together.
-// The arithmetic is exactly that of softmax_core and block_pv_fold.
-template <int BK>
-__device__ __forceinline__ void pipe_stage(f32x16 (&s)[BK / 32], float c, BlockP<BK, false>& Pn,
-                                           const VReads<BK>& vr, const BlockP<BK, false>& Pp, const FoldIn& inp,
-                                           f32x16 (&acc)[kDTiles]) {
-  constexpr int NKT = BK / 32;
-  constexpr int NS = BK / 16;      // 16-key steps (MFMAs) per dim tile
-  constexpr int N = NS * kDTiles;  // slots
-  static_assert(2 * N == 16 * NKT, "two softmax elements per slot");
-  Pn.m_t = block_max<BK>(s, c);
-  const float mu = block_m_use(Pn.m_t);
-  float sub[NKT];                // canonical sum of each sub-tile
-  float lv1 = 0.0f, lv2 = 0.0f;  // pending first / second tree level
-  VRing<BK, false, 2> ring;
-  ring.start(vr);
-  f32x16 ab;
-  sched_fence();
-#pragma unroll
-  for (int i = 0; i < N; ++i) {
-    const int t = i / NS;
-    const int n = i % NS;
-    const int j = i + 1;
-    if (j < N) ring.f[j % 2] = ring.load(vr, j);
-    ab = mfma(ring.f[i % 2], as_bf16x8(Pp.ph[n >> 1][n & 1]), n == 0 ? f32x16{} : ab);
-    // softmax elements 2i, 2i+1 (pair wp of sub-tile kt); the sum tree of
-    // tree16 is reduced as its operands complete
-    const int kt = (2 * i) / 16;
-    const int v = (2 * i) % 16;
-    const int wp = v / 2;
-    const float p0 = block_p(s[kt][v], c, mu);
-    const float p1 = block_p(s[kt][v + 1], c, mu);
-    Pn.ph[kt][v / 8][(v % 8) / 2] = pack_bf16(p0, p1);
-    const float a = p0 + p1;
-    if ((wp & 1) == 0) {
-      lv1 = a;
-    } else {
-      const float b = lv1 + a;
-      if ((wp & 3) == 1) {
-        lv2 = b;
-      } else {
-        const float cc = lv2 + b;
-        if (wp == 3) {
-          sub[kt] = cc;
-        } else {
-          sub[kt] = pair_sum(sub[kt] + cc);
-        }
-      }
-    }
-    if (n == NS - 1) fold_tile(acc[t], ab, inp);  // tile t complete
-    sched_fence();
-  }
-  Pn.l_b = combine_subtiles<NKT>(sub);
-}
-
 // ------------------------------------------------------------ work map --
 
 struct TileMap {
@@ -431,147 +341,6 @@ __device__ __forceinline__ void write_out(const PrefillArgs& a, const TileMap& t
   if (half == 0) a.lse[out_row * a.Hq + tm.head] = fin.lse;
 }
 
-// bf16 output: software-pipelined over blocks.  Iteration j has two stages,
-// each ended by a workgroup barrier:
-//   matrix stage: S_j = K_j Q^T
-//   vector stage: softmax of S_j (vector ALU) interleaved with the PV MFMAs
-//                 and the fold of block j-1 (pipe_stage)
-// so the PV work of every block hides under the softmax of the next one.
-// Registers are the limit (two waves per SIMD, 256 each), so the Q tile of
-// each wave lives in LDS in fragment order (8 KiB per wave, read once per
-// block), K is single-buffered and V double-buffered: LDS holds K_j, V_{j-1},
-// V_j and Q (160 KiB for 128-key blocks).  V_j is loaded from the start of
-// iteration j (its buffer held V_{j-2}) and must land by the vector stage of
-// iteration j+1; K_{j+1} is loaded once every wave has read K_j (the vector
-// stage of iteration j) and must land by the end of that iteration.  The
-// step takes the regions as restrict pointers, so the compiler does not
-// stall LDS reads of one region on the in-flight loads into another.
-template <int BK, bool PAGED>
-__global__ __launch_bounds__(kThreads) void prefill_pipe_kernel(const PrefillArgs a) {
-  using L = TileLayout<BK>;
-  using Ld = BlockLoader<BK, kWaves>;
-  using P = BlockP<BK, false>;
-  __shared__ __attribute__((aligned(16))) char kbuf[L::kKBytes];
-  __shared__ __attribute__((aligned(16))) char vbuf[2 * L::kVBytes];
-  __shared__ __attribute__((aligned(16))) char qbuf[kWaves * 32 * kHeadDim * 2];
-
-  WaveCtx w;
-  wave_setup(a, blockIdx.x, w);
-  const TileMap& tm = w.tm;
-  const int64_t n_kv_blocks = (a.kv_len + BK - 1) / BK;
-  const int64_t nblk = a.causal ? min(n_kv_blocks, (a.pos0 + tm.tile_t1) / BK + 1) : n_kv_blocks;
-
-  FoldState fs{kNegInf, 0.0f};
-  f32x16 acc[kDTiles];
-#pragma unroll
-  for (int dt = 0; dt < kDTiles; ++dt) acc[dt] = f32x16{};
-
-  Ld ld;
-  ld.init(static_cast<int>(w.row_stride));
-  PagedLoader<BK, kWaves> pl;
-  if constexpr (PAGED)
-    pl.init(a.page_table + static_cast<int64_t>(tm.b) * a.max_pages, a.log2_P, a.kv_len, a.num_pages, a.Hkv, tm.hk);
-  // paged: the page ids of block j (ids_cur) and j+1 (ids_next), fetched a
-  // step ahead and before the V loads of the step, so the waits below cover
-  // them and no issue waits for a table read
-  int ids_cur = 0, ids_next = 0;
-  auto issue_k = [&](char* dst, int64_t key0, int ids) {
-    if constexpr (PAGED) {
-      pl.template issue_with<false>(dst, a.k, key0, ids);
-    } else {
-      ld.issue_k(dst, w.krs, key0);
-    }
-  };
-  auto issue_v = [&](char* dst, int64_t key0, int ids) {
-    if constexpr (PAGED) {
-      pl.template issue_with<true>(dst, a.v, key0, ids);
-    } else {
-      ld.issue_v(dst, w.vrs, key0);
-    }
-  };
-  // this lane's Q fragments, step ds at qlane + ds*1024
-  char* const qlane = qbuf + ld.wave * (32 * kHeadDim * 2) + (threadIdx.x & 63) * 16;
-#pragma unroll
-  for (int ds = 0; ds < kDSteps; ++ds) *reinterpret_cast<u32x4*>(qlane + ds * 1024) = __builtin_bit_cast(u32x4, w.qf[ds]);
-  // V buffer 1 stands for block -1 in the first step: zeros
-  for (int i = threadIdx.x; i < L::kVBytes / 16; i += kThreads)
-    *reinterpret_cast<u32x4*>(vbuf + L::kVBytes + 16 * i) = u32x4{0, 0, 0, 0};
-  if constexpr (PAGED) ids_cur = pl.fetch(0);
-  if (nblk > 0) issue_k(kbuf, 0, ids_cur);
-  wait_direct_loads();  // K_0
-  lds_barrier();
-
-  const int kvl = static_cast<int>(a.kv_len);
-  const int qpos = static_cast<int>(tm.qpos);
-  auto cnt = [&](int64_t blk) { return blk < nblk ? Ld::NI : 0; };
-
-  // kc: K_j (read, then refilled with K_{j+1}); vn: V buffer refilled with
-  // V_j; vp: V_{j-1} (read).  Pn/inn: softmax result of block j; Pp/inp: that
-  // of block j-1 (pending pv+fold when pend).
-  auto step = [&](int64_t blk, char* __restrict__ kc, char* __restrict__ vn, const char* __restrict__ vp, P& Pn,
-                  FoldIn& inn, const P& Pp, const FoldIn& inp, bool& pend) {
-    if constexpr (PAGED) ids_next = pl.fetch((blk + 1) * BK);
-    if (blk < nblk) issue_v(vn, blk * BK, ids_cur);
-    const bool sm = blk < nblk && wave_sees<BK>(a, tm, blk);
-    f32x16 s[BK / 32];
-    if (sm) block_scores_q<BK>(kc, qlane, s);
-    const VReads<BK> vr(vp);  // addresses for the vector stage, computed while the MFMAs run
-    sched_fence();
-    wait_loads_leq<Ld::NI>(cnt(blk));  // V_{j-1} landed (V_j may be in flight)
-    lds_barrier();
-    if (blk + 1 < nblk) issue_k(kc, (blk + 1) * BK, ids_next);
-    if (sm && !wave_full<BK>(a, tm, blk)) apply_mask<BK>(s, static_cast<int>(blk * BK), kvl, a.causal, qpos);
-    if (pend && inp.any_move) {
-#pragma unroll
-      for (int dt = 0; dt < kDTiles; ++dt) {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc[dt][v] = acc[dt][v] * inp.f.alpha;
-      }
-    }
-    if (sm || pend) {
-      // One code path for every case: without a block j the scores are all
-      // -inf (p = 0, result unused); without a block j-1 the pending state is
-      // all zero (P = 0, r = beta = 0) and its V buffer holds zeros, so the
-      // fold adds exact zeros.
-      if (!sm) {
-#pragma unroll
-        for (int kt = 0; kt < BK / 32; ++kt) {
-#pragma unroll
-          for (int v = 0; v < 16; ++v) s[kt][v] = kNegInf;
-        }
-      }
-      pipe_stage<BK>(s, a.c, Pn, vr, Pp, inp, acc);
-    }
-    if (sm) {
-      inn = fold_prepare(fs, Pn.m_t, Pn.l_b);
-    } else {
-      Pn = P{};  // keeps the dead state out of the live range
-      inn = FoldIn{};
-    }
-    pend = sm;
-    sched_fence();
-    wait_direct_loads();  // K_{j+1} (and V_j) landed
-    if constexpr (PAGED) {
-      if (blk < nblk && (blk + 1) * BK > a.kv_len) pl.clear_tail(vn, blk * BK, a.kv_len);
-      ids_cur = ids_next;
-    }
-    lds_barrier();
-  };
-
-  P PA{}, PB{};
-  FoldIn ia{}, ib{};
-  bool pend = false;
-  for (int64_t blk = 0; blk <= nblk; ++blk) {
-    const int cb = static_cast<int>(blk & 1);
-    step(blk, kbuf, vbuf + cb * L::kVBytes, vbuf + (cb ^ 1) * L::kVBytes, PA, ia, PB, ib, pend);
-    PB = PA;  // block j becomes the pending block
-    ib = ia;
-  }
-
-  if (!tm.q_ok) return;
-  write_out<false>(a, tm, fs, acc);
-}
-
 // bf16 output, ping-pong schedule.  Waves w and w+4 of the workgroup share a
 // SIMD.  Each wave's work is cut into two kinds of stage that use different
 // units:
@@ -593,7 +362,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pipe_kernel(const PrefillArg
 // and the loads in flight touch different arrays, and does not make the
 // reads wait.  Q stays in registers.  Per block and wave the operations are
 // those of the other fused kernels, so the result is the same bits.
-template <int BK>
+template <int BK, int PG>
 __global__ __launch_bounds__(kThreads) void prefill_pp_kernel(const PrefillArgs a) {
   using L = TileLayout<BK>;
   using Ld = BlockLoader<BK, kWaves / 2>;  // the waves of group 1
@@ -628,6 +397,26 @@ __global__ __launch_bounds__(kThreads) void prefill_pp_kernel(const PrefillArgs 
   sched_fence();  // the Q loads of wave_setup stay ahead of the direct loads
   Ld ld;
   ld.init(static_cast<int>(w.row_stride), wave & 3);
+  // Paged (PG != 0): group 1 gathers K and V through the page table (PG > 0:
+  // the page size is 2^PG, fixed at compile time; PG < 0: any page size).
+  PagedBufLoader<BK, kWaves / 2, (PG > 0 ? PG : 0)> pl;
+  if constexpr (PG != 0)
+    pl.init(a.page_table + static_cast<int64_t>(tm.b) * a.max_pages, a.log2_P, a.kv_len, a.num_pages, a.Hkv, tm.hk,
+            wave & 3);
+  auto issue_k = [&](char* dst, int key0) {
+    if constexpr (PG != 0) {
+      pl.template issue<false>(dst, a.k, key0);
+    } else {
+      ld.issue_k(dst, w.krs, key0);
+    }
+  };
+  auto issue_v = [&](char* dst, int key0) {
+    if constexpr (PG != 0) {
+      pl.template issue<true>(dst, a.v, key0);
+    } else {
+      ld.issue_v(dst, w.vrs, key0);
+    }
+  };
 
   const int kvl = static_cast<int>(a.kv_len);
   const int qpos = static_cast<int>(tm.qpos);
@@ -642,8 +431,8 @@ __global__ __launch_bounds__(kThreads) void prefill_pp_kernel(const PrefillArgs 
   // (i+1)&1 and V_i into the V array of parity i&1.  par = i & 1.
   auto loads = [&](auto par, int i) {
     constexpr int p = decltype(par)::value;
-    if (i + 1 < nblk) ld.issue_k(p ? kb0 : kb1, w.krs, (i + 1) * BK);
-    if (i < nblk) ld.issue_v(p ? vb1 : vb0, w.vrs, i * BK);
+    if (i + 1 < nblk) issue_k(p ? kb0 : kb1, (i + 1) * BK);
+    if (i < nblk) issue_v(p ? vb1 : vb0, i * BK);
   };
   // Matrix stage A_j (par = j & 1): PV + fold of block j-1 from the V array of
   // parity (j-1)&1, then the scores of block j from the K array of parity j&1.
@@ -730,7 +519,7 @@ __global__ __launch_bounds__(kThreads) void prefill_pp_kernel(const PrefillArgs 
     // prologue: K_0 (and the Q rows) landed; then the loads of half-step 0
     // (K_1, V_0), with nothing else in flight, so the compiler's wait
     // counting stays exact
-    if (nblk > 0) ld.issue_k(kb0, w.krs, 0);
+    if (nblk > 0) issue_k(kb0, 0);
     wait_direct_loads();
     lds_barrier();
     loads(I0{}, 0);
@@ -950,10 +739,14 @@ hipError_t launch_t(PrefillArgs a, hipStream_t s) {
   } else if constexpr (F32) {
     hipLaunchKernelGGL((prefill_fused_kernel<BK, F32, PAGED>), dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, s,
                        a);
-  } else if constexpr (PAGED) {
-    hipLaunchKernelGGL((prefill_pipe_kernel<BK, PAGED>), dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, s, a);
   } else {
-    hipLaunchKernelGGL((prefill_pp_kernel<BK>), dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, s, a);
+    if (!PAGED) {
+      hipLaunchKernelGGL((prefill_pp_kernel<BK, 0>), dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, s, a);
+    } else if (a.log2_P == 4) {  // 16-key pages
+      hipLaunchKernelGGL((prefill_pp_kernel<BK, 4>), dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, s, a);
+    } else {
+      hipLaunchKernelGGL((prefill_pp_kernel<BK, -1>), dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, s, a);
+    }
   }
   return hipGetLastError();
 }

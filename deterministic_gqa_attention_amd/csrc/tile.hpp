@@ -126,7 +126,6 @@ struct PagedLoader {
   using L = TileLayout<BK>;
   static constexpr int NI = L::kLoadsPerRegion / NW;
   static_assert(NW % 4 == 0, "swizzle bits must not depend on the load index");
-  static_assert((NI & (NI - 1)) == 0 && NI <= 64, "one id per lane");
   int wave;
   int kbyte0;               // lane's byte offset within its 4-row group (K swizzle)
   int vbyte0;               // the same with the V swizzle
@@ -163,21 +162,6 @@ struct PagedLoader {
     }
   }
 
-  // The page ids of this wave's loads of the block at key0, fetched ahead by
-  // one vector load (lane i < NI: the page of load i), so that issue_with
-  // never waits for a table read: the ids travel with the wave's other
-  // vector loads and are complete once any later load is.
-  __device__ __forceinline__ int fetch(int64_t key0) const {
-    const int i = (threadIdx.x & 63) & (NI - 1);
-    const int idx = min(static_cast<int>((key0 + 4 * (wave + NW * i)) >> log2_P), last_idx);
-    return table[idx];
-  }
-  template <bool V>
-  __device__ __forceinline__ void issue_with(char* dst, const uint16_t* pool, int64_t key0, int ids) const {
-#pragma unroll
-    for (int i = 0; i < NI; ++i) load_one<V>(dst, pool, key0, i, __builtin_amdgcn_readlane(ids, i));
-  }
-
   template <bool V>
   __device__ __forceinline__ void load_one(char* dst, const uint16_t* pool, int64_t key0, int i, int64_t page) const {
     const int n = wave + NW * i;
@@ -196,6 +180,93 @@ struct PagedLoader {
     for (int i = 0; i < NI; ++i) {
       const int n = wave + NW * i;
       if (key0 + 4 * n + (lane >> 4) >= kv_len) *reinterpret_cast<u32x4*>(dst + n * 1024 + lane * 16) = u32x4{0, 0, 0, 0};
+    }
+  }
+};
+
+// Direct buffer->LDS loads of one KV block gathered through a page table,
+// into the layout of BlockLoader, for a loading team of NW waves: each load
+// instruction moves 4 consecutive keys, which lie in one page (page size
+// P >= 4), through a buffer resource over that page's rows below kv_len, so
+// rows at or past kv_len read as zeros (as the contiguous path's do).  Page
+// ids are scalar reads of the table; ids outside [0, num_pages) are clamped
+// into the pool, so a bad table cannot fault (its result is unspecified).
+// LOG2P > 0 fixes the page size at compile time (it must be at least 4*NW
+// keys): then the table entry and the in-page row of every load of a block
+// are constants plus the block's first entry and the wave's row, and a block
+// that ends at or before kv_len takes a short path (whole pages, no clamp of
+// the table index), a few scalar instructions per load.  LOG2P == 0 takes the
+// page size at run time.
+template <int BK, int NW, int LOG2P = 0>
+struct PagedBufLoader {
+  using L = TileLayout<BK>;
+  static constexpr int NI = L::kLoadsPerRegion / NW;
+  static_assert(NW % 4 == 0, "swizzle bits must not depend on the load index");
+  static_assert(LOG2P == 0 || (1 << LOG2P) >= 4 * NW, "a fixed page holds a whole row of the team's loads");
+  int wave;
+  int koff, voff;          // lane's byte offset within its 4-row group (K / V swizzle)
+  const int32_t* table;    // page ids of this sequence
+  int log2_P;
+  int last_idx;            // table index of the page that holds key kv_len-1
+  int max_page;            // num_pages - 1
+  uint32_t page_bytes;     // Hkv * P * 256
+  uint32_t head_bytes;     // hk * P * 256
+  int kv_len;
+
+  __device__ __forceinline__ void init(const int32_t* tab, int lp, int64_t kvl, int64_t pages, int Hkv, int hk,
+                                       int w) {
+    wave = w;
+    const int lane = threadIdx.x & 63;
+    const int g = lane >> 4;
+    const int p = lane & 15;
+    const int r = 4 * wave + g;
+    koff = g * 256 + ((p ^ L::k_swz(r)) << 4);
+    voff = g * 256 + ((p ^ L::v_swz(r)) << 4);
+    table = tab;
+    log2_P = LOG2P > 0 ? LOG2P : lp;
+    last_idx = kvl > 0 ? static_cast<int>((kvl - 1) >> log2_P) : 0;
+    max_page = static_cast<int>((pages < 0x7fffffff ? pages : 0x7fffffff) - 1);
+    page_bytes = static_cast<uint32_t>(Hkv) << (log2_P + 8);
+    head_bytes = static_cast<uint32_t>(hk) << (log2_P + 8);
+    kv_len = static_cast<int>(kvl);
+  }
+
+  __device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const uint16_t* pool, int page, int rows) const {
+    page = page < 0 ? 0 : (page > max_page ? max_page : page);
+    const char* base = reinterpret_cast<const char*>(pool) + head_bytes +
+                       static_cast<uint64_t>(static_cast<uint32_t>(page)) * page_bytes;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, rows * 256, 0x00020000);
+  }
+
+  template <bool V>
+  __device__ __forceinline__ void issue(char* dst, const uint16_t* pool, int key0) const {
+    typedef const __attribute__((address_space(4))) int32_t ctab;
+    if (LOG2P > 0 && key0 + BK <= kv_len) {
+      // whole pages, entries [key0/P, (key0+BK)/P) of the table
+      constexpr int P = 1 << (LOG2P > 0 ? LOG2P : 2);
+      const ctab* t = (ctab*)table + (key0 >> LOG2P);
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int n = wave + NW * i;
+        constexpr int kTeamRows = 4 * NW;  // rows one load index covers across the team
+        const int entry = (kTeamRows * i) >> LOG2P;
+        const int row = ((kTeamRows * i) & (P - 1)) + 4 * wave;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(page_rsrc(pool, t[entry], P), (lds_void*)(dst + n * 1024), 16,
+                                                 V ? voff : koff, row * 256, 0, 0);
+      }
+      return;
+    }
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int n = wave + NW * i;
+      const int key = key0 + 4 * n;
+      const int idx = min(key >> log2_P, last_idx);
+      const int pkey0 = (key >> log2_P) << log2_P;
+      const int left = kv_len - pkey0;
+      const int rows = left <= 0 ? 0 : (left >= (1 << log2_P) ? (1 << log2_P) : left);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(page_rsrc(pool, ((ctab*)table)[idx], rows),
+                                               (lds_void*)(dst + n * 1024), 16, V ? voff : koff,
+                                               (key - pkey0) * 256, 0, 0);
     }
   }
 };

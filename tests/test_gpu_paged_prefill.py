@@ -44,7 +44,7 @@ def _paged(cache, P, seed):
 CASES = [(0, 300), (130, 200), (513, 77), (640, 1)]
 
 
-@pytest.mark.parametrize("block,pages", [(128, (4, 16, 64, 128)), (64, (4, 8, 32, 64))])
+@pytest.mark.parametrize("block,pages", [(128, (4, 16, 64, 128)), (64, (4, 8, 16, 32, 64))])
 @pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])
 def test_paged_equals_contiguous(block, pages, out_dtype):
     B, S, Hq, Hkv = 2, 720, 8, 2

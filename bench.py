@@ -56,10 +56,10 @@ TRACE_CMD = {
     "prefill": "rocprofv3 --kernel-trace --stats -d gpurun_out/prof_prefill -o run --output-format csv -- "
                "python3 bench.py --only prefill --steps 20 --warmup 3",
     "decode": "rocprofv3 --kernel-trace --stats -d gpurun_out/prof_decode -o run --output-format csv -- "
-              "python3 bench.py --only decode --decode-steps 10",
+              "python3 bench.py --only decode --decode-steps 10 --decode-write-only-ref 0",
 }
 PMC_CMD = ("rocprofv3 --pmc {c} -d gpurun_out/pmc_{c}_{m} -o run --output-format csv -- "
-           "python3 bench.py --only {m} --steps 2 --warmup 1 --decode-steps 2")
+           "python3 bench.py --only {m} --steps 2 --warmup 1 --decode-steps 2 --decode-write-only-ref 0")
 PMC_CMD_LM_HEAD = ("rocprofv3 --pmc {c} -d gpurun_out/pmc_{c}_lm_head -o run --output-format csv -- "
                    "python3 bench.py --only lm_head")
 PMC_CMD_MFMA = ("rocprofv3 --pmc GRBM_GUI_ACTIVE SQ_BUSY_CYCLES SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU SQ_INSTS_MFMA "
@@ -390,6 +390,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--decode-steps", type=int, default=25)
+    ap.add_argument("--decode-write-only-ref", type=int, default=1,
+                    help="also time each decode rep after a write-only flush (0: skip, for profiling)")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-reported", action="store_true", help="skip the long-context and chunked-replay legs")
@@ -585,7 +587,15 @@ def decode_leg(args, api, d, dcfg, up, dev, stream):
     max_ctx = dcfg.len_hi
     ws = torch.empty((api.decode_workspace_bytes(dcfg.Hq, dcfg.Hkv, dcfg.batch, max_ctx, block=dcfg.block),),
                      dtype=torch.uint8, device=dev)
-    flush = torch.empty((1 << 30,), dtype=torch.uint8, device=dev)  # > 256 MB last-level cache
+    # Cache flush before each timed call: 1 GiB written, then 1 GiB read, both
+    # far above the 256 MB last-level cache, so no KV byte of the previous call
+    # is served from cache.  The read also drains the dirty lines the write
+    # leaves behind; after a write alone their write-back to HBM lands inside
+    # the timed call (measured: write only 521 us, write + read 458 us, read
+    # only 459 us, no flush 483 us per call), which is traffic the decode does
+    # not make.  The write-only figure is reported beside the main one.
+    flush_w = torch.empty((1 << 30,), dtype=torch.uint8, device=dev)
+    flush_r = torch.ones((1 << 28,), dtype=torch.float32, device=dev)
     kv_bytes = gen.decode_kv_bytes(host_lens, dcfg.Hkv, dcfg.D)
     used_pages = int((-(-host_lens.astype(np.int64) // dcfg.page_size)).sum())
     other = dcfg.batch * dcfg.Hq * dcfg.D * 2 * 2 + dcfg.batch * dcfg.Hq * 4 + used_pages * 4 + dcfg.batch * 4
@@ -593,9 +603,10 @@ def decode_leg(args, api, d, dcfg, up, dev, stream):
     for _ in range(2):
         api.decode_paged(qq, kp, vp, table, lens, block=dcfg.block, max_context_len=max_ctx,
                          host_ctx_lens=host_lens, workspace=ws)
-    times = []
-    for _ in range(args.decode_steps):
-        flush.fill_(1)
+    def timed_call(read_after_write):
+        flush_w.fill_(1)
+        if read_after_write:
+            flush_r.sum()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(stream)
@@ -603,16 +614,25 @@ def decode_leg(args, api, d, dcfg, up, dev, stream):
                          host_ctx_lens=host_lens, workspace=ws)
         e1.record(stream)
         torch.cuda.synchronize()
-        times.append(e0.elapsed_time(e1))
+        return e0.elapsed_time(e1)
+
+    times, times_w = [], []
+    for _ in range(args.decode_steps):
+        times.append(timed_call(True))
+        if args.decode_write_only_ref:
+            times_w.append(timed_call(False))
     dms = float(np.median(times))
+    dms_w = float(np.median(times_w)) if times_w else None
     gbs = kv_bytes / (dms * 1e-3) / 1e9
     ach = alg_bytes / (dms * 1e-3) / 1e9
     decode = {"value": round(gbs, 1), "unit": "GB/s", "ms": round(dms, 4), "kv_bytes": kv_bytes,
               "workload": "paged decode, 64 seqs, len U[512,16384] (sum %d), Hq=32 Hkv=8 D=128, page 16, "
                           "1M-slot pool, 128-key blocks, bf16 out" % int(host_lens.sum()),
+              "flush": "1 GiB written then 1 GiB read before each timed call (median of %d)" % len(times),
+              "ms_after_write_only_flush": round(dms_w, 4) if dms_w else None,
               "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                            "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": profile_traffic(DECODE_PROFILE)}}
-    log(f"decode {dms:.3f} ms, {gbs:.0f} GB/s KV")
+    log(f"decode {dms:.3f} ms, {gbs:.0f} GB/s KV" + (f" (after a write-only flush {dms_w:.3f} ms)" if dms_w else ""))
     return decode
 
 
@@ -737,7 +757,9 @@ def summarize_profiles(d):
         f"Drawn lengths sum to {int(lens.sum())} tokens; K+V bytes read {kv}; algorithmic bytes per decode call "
         f"{dec_alg} (KV, Q, Out, LSE, used page-table entries, lengths).",
         "",
-        "Kernel trace (decode = items kernel + fold kernel; caches flushed by a 1 GiB fill between calls):",
+        "Kernel trace (decode = items kernel + fold kernel; before each timed call 1 GiB is written, then 1 GiB read,",
+        "so no KV byte is cache-served and no dirty line of the flush is written back inside the call; the first",
+        "two calls are unflushed warm-ups):",
         "",
         "    " + TRACE_CMD["decode"],
         "",

@@ -48,13 +48,16 @@ PREFILL_PROFILE = os.path.join(PROFILES, "prefill_kernel_b4_s4096.md")
 DECODE_PROFILE = os.path.join(PROFILES, "decode_paged_64seq.md")
 BACKWARD_PROFILE = os.path.join(PROFILES, "backward_b4_s4096.md")
 LM_HEAD_PROFILE = os.path.join(PROFILES, "lm_head_logprobs_t64_v151936.md")
+TIMED_STEPS = 20  # --steps of the prefill profiling commands below
+BACKWARD_TIMED_STEPS = 10  # --steps of the backward trace command
+LM_HEAD_TIMED_REPS = 5  # timed calls of the lm_head leg
 TRACE_CMD = {
     "lm_head": "rocprofv3 --kernel-trace --stats -d gpurun_out/prof_lm_head -o run --output-format csv -- "
                "python3 bench.py --only lm_head",
     "backward": "rocprofv3 --kernel-trace --stats -d gpurun_out/prof_backward -o run --output-format csv -- "
                 "python3 bench.py --only backward --steps 10",
     "prefill": "rocprofv3 --kernel-trace --stats -d gpurun_out/prof_prefill -o run --output-format csv -- "
-               "python3 bench.py --only prefill --steps 20 --warmup 3",
+               "python3 bench.py --only prefill --steps 20",
     "decode": "rocprofv3 --kernel-trace --stats -d gpurun_out/prof_decode -o run --output-format csv -- "
               "python3 bench.py --only decode --decode-steps 10 --decode-write-only-ref 0",
 }
@@ -64,9 +67,32 @@ PMC_CMD_LM_HEAD = ("rocprofv3 --pmc {c} -d gpurun_out/pmc_{c}_lm_head -o run --o
                    "python3 bench.py --only lm_head")
 PMC_CMD_MFMA = ("rocprofv3 --pmc GRBM_GUI_ACTIVE SQ_BUSY_CYCLES SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU SQ_INSTS_MFMA "
                 "SQ_WAVE_CYCLES -d gpurun_out/pmc_mfma_prefill -o run --output-format csv -- "
-                "python3 bench.py --only prefill --steps 2 --warmup 1")
+                "python3 bench.py --only prefill --steps 20")
 PMC_CMD_BACKWARD = ("rocprofv3 --pmc {c} -d gpurun_out/pmc_{c}_backward -o run --output-format csv -- "
                     "python3 bench.py --only backward --steps 2")
+
+
+SETTLE_MS = 100.0  # untimed dense work before a reported leg's timing
+
+
+def settle(fn, ms=SETTLE_MS, cap=4096):
+    """Run fn, untimed, until about `ms` milliseconds of wall time have passed
+    (at least once).  After an idle spell the GPU comes back at a high clock,
+    overshoots its power budget and is throttled for the next few tens of
+    milliseconds of dense work before it settles; timing that starts at once
+    measures the transient (prefill B=4 S=4096: 0.675 ms per launch for the
+    20 launches after 3 warm-ups, 0.565-0.59 ms from about the 50th launch on,
+    0.69 ms again after 2 s idle)."""
+    import torch
+
+    t0 = time.perf_counter()
+    for n in range(cap):
+        fn()
+        if n % 4 == 3 or n == 0:
+            torch.cuda.synchronize()
+            if time.perf_counter() - t0 >= ms * 1e-3:
+                break
+    torch.cuda.synchronize()
 
 
 def log(msg):
@@ -191,8 +217,7 @@ def reported_legs(api, up, stream, cpu_seconds=None):
     import torch
 
     def timed(fn, reps):
-        fn()
-        torch.cuda.synchronize()
+        settle(fn)
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(stream)
@@ -296,9 +321,7 @@ def backward_leg(api, cfg, qd, kd, vd, up, stream, steps, cpu_q=None):
     def call():
         api.backward(qd, kd, vd, out, lse, do, scale=cfg.softmax_scale, dq=dq, dk=dk, dv=dv, workspace=ws)
 
-    for _ in range(2):
-        call()
-    torch.cuda.synchronize()
+    settle(call)
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record(stream)
@@ -351,8 +374,7 @@ def lm_head_leg(api, up, stream, reps=5, cpu=False):
     x = up(gen.draw_bf16(1000 * 4 + 11, (T, H)))
     tok = torch.from_numpy(gen.lm_tokens(T, V)).to(stream.device)
     ws = api.alloc_workspace(api.lm_head_workspace_bytes(T, V), stream.device)
-    api.lm_head_logprobs(x, w, tok, workspace=ws)
-    torch.cuda.synchronize()
+    settle(lambda: api.lm_head_logprobs(x, w, tok, workspace=ws))
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record(stream)
@@ -388,7 +410,8 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=100,
+                    help="untimed prefill launches first (~60 ms: the clock settles after idle)")
     ap.add_argument("--decode-steps", type=int, default=25)
     ap.add_argument("--decode-write-only-ref", type=int, default=1,
                     help="also time each decode rep after a write-only flush (0: skip, for profiling)")
@@ -400,7 +423,12 @@ def main():
                     help="run one leg only (for profiler and counter runs)")
     ap.add_argument("--summarize", metavar="DIR", default=None,
                     help="write profiles/*.md from the rocprofv3 CSVs under DIR (no GPU work)")
+    ap.add_argument("--profile-commands", action="store_true",
+                    help="print the rocprofv3 commands whose output --summarize reads, one per line")
     args = ap.parse_args()
+    if args.profile_commands:
+        print("\n".join(profile_commands()))
+        return
     if args.summarize:
         summarize_profiles(args.summarize)
         return
@@ -663,6 +691,29 @@ def _read_csv(path):
         return list(csv.DictReader(f))
 
 
+def profile_commands():
+    """Every rocprofv3 command the profiles/*.md summaries quote, in run order
+    (kernel traces first, then one counter per run)."""
+    cmds = [TRACE_CMD[m] for m in ("prefill", "decode", "backward", "lm_head")]
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        cmds += [PMC_CMD.format(c=c, m=m) for m in ("prefill", "decode", "copy")]
+        cmds += [PMC_CMD_LM_HEAD.format(c=c), PMC_CMD_BACKWARD.format(c=c)]
+    return cmds + [PMC_CMD_MFMA]
+
+
+def _last_dispatches(d, mode, parts, n):
+    """(name, n, avg us, min us, max us) per kernel over its last n dispatches
+    in the kernel trace under d/prof_<mode>: the timed launches, after the
+    untimed warm-up ones."""
+    trace = sorted(_read_csv(os.path.join(d, f"prof_{mode}", "run_kernel_trace.csv")),
+                   key=lambda r: int(r["Start_Timestamp"]))
+    per = {}
+    for r in trace:
+        if any(p in r["Kernel_Name"] for p in parts):
+            per.setdefault(r["Kernel_Name"], []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    return [(k, len(v[-n:]), float(np.mean(v[-n:])), min(v[-n:]), max(v[-n:])) for k, v in per.items()]
+
+
 def _pmc_mean(d, counter, mode, name_part):
     """Mean counter value (KiB per dispatch) of the kernels whose name contains name_part."""
     path = os.path.join(d, f"pmc_{counter}_{mode}", "run_counter_collection.csv")
@@ -712,18 +763,28 @@ def summarize_profiles(d):
     st = stats_rows("prefill", ["prefill_pp_kernel"])
     fk, wk, fb, wb, n = counters("prefill", "prefill_pp_kernel")
     name, calls, avg, mn, mx = st[0]
+    trace = _read_csv(os.path.join(d, "prof_prefill", "run_kernel_trace.csv"))
+    durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+            for r in sorted(trace, key=lambda r: int(r["Start_Timestamp"])) if "prefill_pp_kernel" in r["Kernel_Name"]]
+    timed = durs[-TIMED_STEPS:]
+    t_avg = float(np.mean(timed))
     flops = cfg.flops()
+
+    def row(label, c, a, lo, hi):
+        return (f"| {label} | {c} | {a:.1f} | {lo:.1f} | {hi:.1f} | {flops / (a * 1e-6) / 1e12:.1f} | "
+                f"{flops / (a * 1e-6) / 1e12 / PEAK_BF16_TFLOPS:.4f} |")
+
     lines = [
         "# Prefill kernel, causal B=4 S=4096 Hq=32 Hkv=8 D=128, 128-key blocks, bf16 out",
         "",
-        "Kernel trace (all dispatches are the timed workload):",
+        f"Kernel trace (100 untimed warm-up launches, then the {TIMED_STEPS} timed ones):",
         "",
         "    " + TRACE_CMD["prefill"],
         "",
-        "| kernel | calls | avg us | min us | max us | TFLOP/s at avg | frac of 2500 |",
+        "| dispatches | calls | avg us | min us | max us | TFLOP/s at avg | frac of 2500 |",
         "|---|---|---|---|---|---|---|",
-        f"| `{name}` | {calls} | {avg:.1f} | {mn:.1f} | {mx:.1f} | {flops / (avg * 1e-6) / 1e12:.1f} | "
-        f"{flops / (avg * 1e-6) / 1e12 / PEAK_BF16_TFLOPS:.4f} |",
+        row(f"`{name}`, the {TIMED_STEPS} timed", len(timed), t_avg, min(timed), max(timed)),
+        row("all, warm-up included (the --stats summary)", calls, avg, mn, mx),
         "",
         f"Algorithmic work per launch: {flops:.6e} flop (4·D·Hq·B·S(S+1)/2); algorithmic HBM bytes "
         f"{pre_alg} (Q, K, V in; Out bf16, LSE out).",
@@ -809,7 +870,7 @@ def summarize_mfma(d, src):
             continue
         e = per.setdefault(r["Dispatch_Id"], {"_ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
         e[r["Counter_Name"]] = e.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
-    runs = list(per.values())
+    runs = [per[k] for k in sorted(per, key=int)][-TIMED_STEPS:]  # the timed launches, after the warm-up
     mean = {k: float(np.mean([x[k] for x in runs])) for k in runs[0]}
     cfg = gen.CFG2
     n_xcd, n_simd = 8, 1024
@@ -821,7 +882,8 @@ def summarize_mfma(d, src):
         "",
         "    " + PMC_CMD_MFMA,
         "",
-        f"Mean over {len(runs)} dispatches of `prefill_pp_kernel<128>`:",
+        f"Mean over the last {len(runs)} dispatches of `prefill_pp_kernel<128, 0>` (the timed launches; the "
+        "100 before them are the warm-up):",
         "",
         "| counter | value per dispatch |",
         "|---|---|",
@@ -851,9 +913,7 @@ def summarize_lm_head(d, f_fetch, f_write, header, src):
     T, H, V = 64, 4096, gen.LM_VOCAB
     flops = 2.0 * T * V * H
     alg_bytes = V * H * 4 + T * H * 2 + T * 4 * 3
-    rows = _read_csv(os.path.join(d, "prof_lm_head", "run_kernel_stats.csv"))
-    kern = [(r["Name"], int(r["Calls"]), float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
-             float(r["MaxNs"]) / 1e3) for r in rows if "lmh_" in r["Name"]]
+    kern = _last_dispatches(d, "lm_head", ["lmh_"], LM_HEAD_TIMED_REPS)
     kern.sort(key=lambda r: 0 if "partial" in r[0] else 1)
     total_us = sum(r[2] for r in kern)
 
@@ -866,7 +926,8 @@ def summarize_lm_head(d, f_fetch, f_write, header, src):
     lines = [
         "# Selected log-probs through the FP32 lm_head: 64 tokens, H = 4096 (bf16 x), V = 151936",
         "",
-        "Kernel trace (two launches per call: logits with per-block log-sum-exp partials, then the ordered fold):",
+        "Kernel trace (two launches per call: logits with per-block log-sum-exp partials, then the ordered fold; "
+        f"the figures are over the {LM_HEAD_TIMED_REPS} timed calls, after about 100 ms of untimed warm-up calls):",
         "",
         "    " + TRACE_CMD["lm_head"],
         "",
@@ -903,9 +964,7 @@ def summarize_lm_head(d, f_fetch, f_write, header, src):
 def summarize_backward(d, f_fetch, f_write, header, src):
     """profiles/backward_b4_s4096.md from the backward kernel trace and counters."""
     cfg = gen.CFG2
-    rows = _read_csv(os.path.join(d, "prof_backward", "run_kernel_stats.csv"))
-    kern = [(r["Name"], int(r["Calls"]), float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
-             float(r["MaxNs"]) / 1e3) for r in rows if "bwd_" in r["Name"]]
+    kern = _last_dispatches(d, "backward", ["bwd_"], BACKWARD_TIMED_STEPS)
     order = {"bwd_dq": 0, "bwd_dkdv": 1}
     kern.sort(key=lambda r: min(v for k, v in order.items() if k in r[0]))
     fwd = cfg.flops()
@@ -925,7 +984,8 @@ def summarize_backward(d, f_fetch, f_write, header, src):
     lines = [
         "# Backward (dQ, dK, dV), causal B=4 S=4096 Hq=32 Hkv=8 D=128, bf16 in, fp32 gradients",
         "",
-        "Kernel trace (two launches per backward call: dQ, which also writes Delta per row, then dK/dV):",
+        "Kernel trace (two launches per backward call: dQ, which also writes Delta per row, then dK/dV; the "
+        f"figures are over the {BACKWARD_TIMED_STEPS} timed calls, after about 100 ms of untimed warm-up calls):",
         "",
         "    " + TRACE_CMD["backward"],
         "",

@@ -369,7 +369,8 @@ rla_status rla_attn_prefill_paged(const rla_attn_params* p, const void* q_chunk,
   if (static_cast<int64_t>(max_pages_per_seq) * page_size < kv_len)
     return fail(RLA_ERR_BAD_SHAPE, "max_pages_per_seq*page_size=%lld does not cover cache_len+chunk_len=%lld",
                 (long long)max_pages_per_seq * page_size, (long long)kv_len);
-  if (kv_len > 0x7fffffff) return fail(RLA_ERR_BAD_SHAPE, "cache_len+chunk_len exceeds int32 positions");
+  // key positions and block starts (plus one block) stay inside int32 in the kernels
+  if (kv_len > (1 << 30)) return fail(RLA_ERR_BAD_SHAPE, "cache_len+chunk_len=%lld exceeds 2^30", (long long)kv_len);
   const int Hq = p->num_q_heads, D = rla::kHeadDimPublic;
   if (!fits_32bit_offsets(chunk_len, Hq))
     return fail(RLA_ERR_UNSUPPORTED, "chunk too long: one head's query rows must span < 2 GiB");

@@ -166,8 +166,8 @@ size_t rla_chunked_workspace_bytes(const rla_attn_params* p, int32_t batch, int3
  * [num_pages][Hkv][page_size][128] bf16 already holding the chunk's keys;
  * page_table [batch][max_pages_per_seq] int32 (device).  page_size must be a
  * power of two with 4 <= page_size <= kv_block_size (one load instruction
- * covers 4 consecutive keys of one page), and max_pages_per_seq * page_size
- * must cover cache_len + chunk_len.  A page id outside [0, num_pages) is
+ * covers 4 consecutive keys of one page), max_pages_per_seq * page_size
+ * must cover cache_len + chunk_len, and cache_len + chunk_len <= 2^30.  A page id outside [0, num_pages) is
  * clamped into that range before use, so a bad table cannot fault, but its
  * result is unspecified.  The result is bit for bit that of
  * rla_attn_prefill_chunked over the same keys, whatever the page layout.

@@ -123,6 +123,8 @@ def test_paged_prefill_rejects_bad_args(lib):
     assert "max_pages_per_seq" in lib.rla_last_error().decode()
     assert call(64, 16, 8, 1, 0, 0) == 2                     # empty chunk
     assert call(0, 16, 8, 1, 16, 0) == 2                     # empty pool
+    assert call(64, 16, 1 << 27, 1, 16, (1 << 30) - 8) == 2  # cache_len + chunk_len past 2^30
+    assert "2^30" in lib.rla_last_error().decode()
 
 
 def _shard(blocks, q_begin=0, q_count=16, n_parts=None, rows=16):

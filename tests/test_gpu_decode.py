@@ -164,6 +164,25 @@ def test_page_sizes_bitwise(block, pages):
         assert_bitwise(l, ref_l, f"page size {P} LSE")
 
 
+@pytest.mark.parametrize("block", [64, 128])
+def test_out_of_range_page_ids_are_clamped(block):
+    """Ids below 0 read page 0 and ids at or past num_pages read the last
+    page: the same bits as the table with those ids clamped."""
+    d = gen.decode_inputs(SMALL, lengths=SMALL_LENS)
+    n_pages = d["k_pool"].shape[0]
+    bad, clamped = d["page_table"].copy(), d["page_table"].copy()
+    # sequence 6 (700 keys, 44 pages) and sequence 4 (129 keys)
+    for (s, i), (b_id, c_id) in zip([(6, 0), (6, 9), (6, 43), (4, 8)],
+                                    [(-1, 0), (n_pages, n_pages - 1), (1 << 30, n_pages - 1), (-(1 << 30), 0)]):
+        bad[s, i] = b_id
+        clamped[s, i] = c_id
+    say(f"[decode] out-of-range page ids block={block}")
+    ro, rl = _decode(dict(d, page_table=clamped), SMALL, block=block, out_dtype=torch.float32)
+    o, l = _decode(dict(d, page_table=bad), SMALL, block=block, out_dtype=torch.float32)
+    assert_bitwise(o, ro, "Out with out-of-range ids")
+    assert_bitwise(l, rl, "LSE with out-of-range ids")
+
+
 def test_empty_context():
     d = gen.decode_inputs(SMALL, lengths=np.array([0, 5, 0], np.int32))
     say("[decode] zero-length contexts")

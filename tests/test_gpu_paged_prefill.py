@@ -41,7 +41,7 @@ def _paged(cache, P, seed):
     return pool, table
 
 
-CASES = [(0, 300), (130, 200), (513, 77), (640, 1)]
+CASES = [(0, 300), (130, 200), (513, 77), (640, 1), (128, 128)]  # the last ends on a block boundary
 
 
 @pytest.mark.parametrize("block,pages", [(128, (4, 16, 64, 128)), (64, (4, 8, 16, 32, 64))])
@@ -102,3 +102,31 @@ def test_paged_parity_with_oracle():
     torch.cuda.synchronize()
     ro, rl = oracle.attention(q[:, c0:], k, v, scale=1 / np.sqrt(128), pos0=c0, kv_len=c0 + C)
     check_parity(host_f64(o).reshape(C, 8, 128), host_f64(l).reshape(C, 8), ro, rl, f32_out=True, what="paged")
+
+
+@pytest.mark.parametrize("P,block,out_dtype", [(16, 128, torch.bfloat16), (32, 128, torch.bfloat16),
+                                               (16, 64, torch.float32)], ids=["p16-bf16", "p32-bf16", "p16-fp32"])
+def test_out_of_range_page_ids_are_clamped(P, block, out_dtype):
+    """Ids below 0 read page 0 and ids at or past num_pages read the last
+    page: the same bits as the table with those ids clamped."""
+    B, S, Hq, Hkv = 1, 400, 8, 2
+    q, k, v = _rand(60, (B, S, Hq, 128)), _rand(61, (B, S, Hkv, 128)), _rand(62, (B, S, Hkv, 128))
+    kp, table = _paged(k, P, 2000 + P)
+    vp, _ = _paged(v, P, 2000 + P)
+    # finite values in the unused pages, which a clamped id may land on
+    kp = np.where(kp == BF16_NAN, np.uint16(0x3F80), kp)
+    vp = np.where(vp == BF16_NAN, np.uint16(0x3F80), vp)
+    n_pages = kp.shape[0]
+    bad, clamped = table.copy(), table.copy()
+    for i, (b_id, c_id) in enumerate([(-3, 0), (n_pages + 10, n_pages - 1), (-(1 << 30), 0),
+                                      (1 << 30, n_pages - 1)]):
+        bad[0, 2 + 3 * i] = b_id
+        clamped[0, 2 + 3 * i] = c_id
+    qc = dev_bf16(q[:, 100:])
+    say(f"[paged] out-of-range page ids P={P} block={block} out={out_dtype}")
+    ro, rl = api.prefill_paged(qc, dev_bf16(kp), dev_bf16(vp), dev_i32(clamped), cache_len=100, block=block,
+                               out_dtype=out_dtype)
+    o, l = api.prefill_paged(qc, dev_bf16(kp), dev_bf16(vp), dev_i32(bad), cache_len=100, block=block,
+                             out_dtype=out_dtype)
+    assert_bitwise(o, ro, "Out with out-of-range ids")
+    assert_bitwise(l, rl, "LSE with out-of-range ids")

@@ -1,5 +1,5 @@
 """Bitwise invariances of the GPU path (max abs 0.0 on Out and LSE):
-batch composition, chunk size, context-parallel split (contiguous and zigzag),
+a row's independence of every other query row, batch composition, chunk size, context-parallel split (contiguous and zigzag),
 fused vs emit+merge, arrival order of partial states, repeat runs.  Plus a
 parity check of the chunked path against the oracle.
 """
@@ -115,6 +115,29 @@ def test_batch_composition():
         so, sl = api.prefill(qd[b:b + 1].contiguous(), kd[b:b + 1].contiguous(), vd[b:b + 1].contiguous(), block=128)
         assert_bitwise(so[0], bo[b], f"seq {b} alone vs batch Out")
         assert_bitwise(sl[0], bl[b], f"seq {b} alone vs batch LSE")
+
+
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])
+def test_row_independent_of_other_rows(out_dtype):
+    """A row's bits depend on its own query and the keys it sees only: every
+    other query row and every other q head (its MFMA tile neighbours, the
+    other rows of its workgroup and the other heads of its kv group) redrawn,
+    the kept rows give the same Out and LSE.  Kept rows sit at tile edges and
+    inside tiles, on and off the causal diagonal, and in the ragged tail."""
+    B, S, Hq, Hkv = 1, 300, 8, 2
+    q, k, v = _rand(71, (B, S, Hq, 128)), _rand(72, (B, S, Hkv, 128)), _rand(73, (B, S, Hkv, 128))
+    keep = [0, 1, 31, 32, 63, 64, 127, 128, 150, 255, 256, 299]
+    head = 5
+    q2 = _rand(74, (B, S, Hq, 128), scale=3.0)
+    q2[:, keep, head] = q[:, keep, head]
+    kd, vd = dev_bf16(k), dev_bf16(v)
+    say(f"[invariance] row independence out={out_dtype}")
+    for block in (64, 128):
+        o1, l1 = api.prefill(dev_bf16(q), kd, vd, block=block, out_dtype=out_dtype)
+        o2, l2 = api.prefill(dev_bf16(q2), kd, vd, block=block, out_dtype=out_dtype)
+        assert_bitwise(o2[:, keep, head], o1[:, keep, head], f"block {block} kept rows Out")
+        assert_bitwise(l2[:, keep, head], l1[:, keep, head], f"block {block} kept rows LSE")
+        assert not torch.equal(o2[:, 2, head], o1[:, 2, head]), "a redrawn row should change"
 
 
 def _replay(qd, kd, vd, chunk, *, block, out_dtype=torch.bfloat16):

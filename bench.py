@@ -52,23 +52,23 @@ TIMED_STEPS = 20  # --steps of the prefill profiling commands below
 BACKWARD_TIMED_STEPS = 10  # --steps of the backward trace command
 LM_HEAD_TIMED_REPS = 5  # timed calls of the lm_head leg
 TRACE_CMD = {
-    "lm_head": "rocprofv3 --kernel-trace --stats -d gpurun_out/prof_lm_head -o run --output-format csv -- "
+    "lm_head": "rocprofv3 --kernel-trace --stats -d rocprof_out/prof_lm_head -o run --output-format csv -- "
                "python3 bench.py --only lm_head",
-    "backward": "rocprofv3 --kernel-trace --stats -d gpurun_out/prof_backward -o run --output-format csv -- "
+    "backward": "rocprofv3 --kernel-trace --stats -d rocprof_out/prof_backward -o run --output-format csv -- "
                 "python3 bench.py --only backward --steps 10",
-    "prefill": "rocprofv3 --kernel-trace --stats -d gpurun_out/prof_prefill -o run --output-format csv -- "
+    "prefill": "rocprofv3 --kernel-trace --stats -d rocprof_out/prof_prefill -o run --output-format csv -- "
                "python3 bench.py --only prefill --steps 20",
-    "decode": "rocprofv3 --kernel-trace --stats -d gpurun_out/prof_decode -o run --output-format csv -- "
+    "decode": "rocprofv3 --kernel-trace --stats -d rocprof_out/prof_decode -o run --output-format csv -- "
               "python3 bench.py --only decode --decode-steps 10 --decode-write-only-ref 0",
 }
-PMC_CMD = ("rocprofv3 --pmc {c} -d gpurun_out/pmc_{c}_{m} -o run --output-format csv -- "
+PMC_CMD = ("rocprofv3 --pmc {c} -d rocprof_out/pmc_{c}_{m} -o run --output-format csv -- "
            "python3 bench.py --only {m} --steps 2 --warmup 1 --decode-steps 2 --decode-write-only-ref 0")
-PMC_CMD_LM_HEAD = ("rocprofv3 --pmc {c} -d gpurun_out/pmc_{c}_lm_head -o run --output-format csv -- "
+PMC_CMD_LM_HEAD = ("rocprofv3 --pmc {c} -d rocprof_out/pmc_{c}_lm_head -o run --output-format csv -- "
                    "python3 bench.py --only lm_head")
 PMC_CMD_MFMA = ("rocprofv3 --pmc GRBM_GUI_ACTIVE SQ_BUSY_CYCLES SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU SQ_INSTS_MFMA "
-                "SQ_WAVE_CYCLES -d gpurun_out/pmc_mfma_prefill -o run --output-format csv -- "
+                "SQ_WAVE_CYCLES -d rocprof_out/pmc_mfma_prefill -o run --output-format csv -- "
                 "python3 bench.py --only prefill --steps 20")
-PMC_CMD_BACKWARD = ("rocprofv3 --pmc {c} -d gpurun_out/pmc_{c}_backward -o run --output-format csv -- "
+PMC_CMD_BACKWARD = ("rocprofv3 --pmc {c} -d rocprof_out/pmc_{c}_backward -o run --output-format csv -- "
                     "python3 bench.py --only backward --steps 2")
 
 

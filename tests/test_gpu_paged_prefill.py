@@ -130,3 +130,29 @@ def test_out_of_range_page_ids_are_clamped(P, block, out_dtype):
                              out_dtype=out_dtype)
     assert_bitwise(o, ro, "Out with out-of-range ids")
     assert_bitwise(l, rl, "LSE with out-of-range ids")
+
+
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])
+def test_non_causal_chunk_parity_and_paged(out_dtype):
+    """A non-causal chunk (every query sees all cache_len + chunk_len keys,
+    also those of later chunk positions): parity of the contiguous chunked
+    path with the oracle, and the paged path (16- and 32-key pages) equal to
+    it bit for bit."""
+    B, S, Hq, Hkv = 2, 330, 8, 2
+    c0, C = 200, 130
+    q, k, v = _rand(63, (B, S, Hq, 128)), _rand(64, (B, S, Hkv, 128)), _rand(65, (B, S, Hkv, 128))
+    qc = dev_bf16(q[:, c0:c0 + C])
+    say(f"[paged] non-causal chunk cache={c0} chunk={C} out={out_dtype}")
+    ro, rl = api.prefill_chunked(qc, dev_bf16(k), dev_bf16(v), cache_len=c0, block=128, out_dtype=out_dtype,
+                                 causal=False)
+    torch.cuda.synchronize()
+    eo, el = oracle.attention(q[:, c0:c0 + C], k, v, scale=1 / np.sqrt(128), pos0=c0, kv_len=c0 + C, causal=False)
+    check_parity(host_f64(ro).reshape(B * C, Hq, 128), host_f64(rl).reshape(B * C, Hq), eo, el,
+                 f32_out=out_dtype == torch.float32, what="non-causal chunk")
+    for P in (16, 32):
+        kp, table = _paged(k, P, 3000 + P)
+        vp, _ = _paged(v, P, 3000 + P)
+        o, l = api.prefill_paged(qc, dev_bf16(kp), dev_bf16(vp), dev_i32(table), cache_len=c0, block=128,
+                                 out_dtype=out_dtype, causal=False)
+        assert_bitwise(o, ro, f"P={P} non-causal Out")
+        assert_bitwise(l, rl, f"P={P} non-causal LSE")

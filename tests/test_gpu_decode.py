@@ -183,6 +183,22 @@ def test_out_of_range_page_ids_are_clamped(block):
     assert_bitwise(l, rl, "LSE with out-of-range ids")
 
 
+def test_device_lengths_above_max_context_are_clamped():
+    """A device context length above max_context_len attends only the first
+    max_context_len keys (the bits of the same call with the lengths clamped);
+    host lengths above it are rejected before any launch."""
+    d = gen.decode_inputs(SMALL, lengths=SMALL_LENS)
+    cap = 300  # SMALL_LENS holds 700 and lengths on both sides of it
+    say(f"[decode] device lengths above max_context_len={cap}")
+    o, l = _decode(d, SMALL, block=128, out_dtype=torch.float32, max_ctx=cap, host_lens=False)
+    dc = dict(d, ctx_lens=np.minimum(d["ctx_lens"], cap).astype(np.int32))
+    ro, rl = _decode(dc, SMALL, block=128, out_dtype=torch.float32, max_ctx=cap, host_lens=False)
+    assert_bitwise(o, ro, "Out with lengths above max_context_len")
+    assert_bitwise(l, rl, "LSE with lengths above max_context_len")
+    with pytest.raises(Exception, match="outside"):
+        _decode(d, SMALL, block=128, out_dtype=torch.float32, max_ctx=cap, host_lens=True)
+
+
 def test_empty_context():
     d = gen.decode_inputs(SMALL, lengths=np.array([0, 5, 0], np.int32))
     say("[decode] zero-length contexts")

@@ -341,13 +341,21 @@ def backward_leg(api, cfg, qd, kd, vd, up, stream, steps, cpu_q=None):
     return res
 
 
-def backward_cpu_baseline(cfg, q, k, v, do, n_rows=48):
+def backward_cpu_baseline(cfg, q, k, v, do, seconds=10.0, probe_rows=48):
     """The FP64 oracle's backward on a seeded sample of query rows of the same
     workload (their complete dQ and their dK/dV terms), in algorithmic flops:
-    10*D per visible (row, key) pair and q head."""
+    10*D per visible (row, key) pair and q head.  A 48-row probe sizes the
+    timed sample to about `seconds` of host work."""
     import oracle
-    rng = np.random.Generator(np.random.PCG64(77))
-    rows = np.unique(rng.integers(0, cfg.B * cfg.S, n_rows))
+
+    def sample(n):
+        rng = np.random.Generator(np.random.PCG64(77))
+        return np.unique(rng.integers(0, cfg.B * cfg.S, n))
+
+    t0 = time.perf_counter()
+    oracle.attention_backward(q, k, v, do, scale=cfg.softmax_scale, rows=sample(probe_rows))
+    per_row = (time.perf_counter() - t0) / probe_rows
+    rows = sample(int(min(cfg.B * cfg.S, max(probe_rows, seconds / max(per_row, 1e-6)))))
     t = rows % cfg.S
     flops = float(np.sum(10.0 * cfg.D * cfg.Hq * (t + 1)))
     t0 = time.perf_counter()
@@ -393,14 +401,14 @@ def lm_head_leg(api, up, stream, reps=5, cpu=False):
            "workload": "selected log-probs, 64 tokens x H=4096 bf16 through an fp32 lm_head of 151936 rows"}
     if cpu:
         import oracle
-        n = 8  # a bounded sample: the first 8 of the 64 tokens
+        n = T  # every token: about 3 s of host work
         xs = x[:n].view(torch.int16).cpu().numpy().view(np.uint16)
         t0 = time.perf_counter()
         oracle.lm_head_logprobs(xs, w_host, gen.lm_tokens(T, V)[:n])
         dt = time.perf_counter() - t0
         f = 2.0 * n * V * H
         res["cpu_baseline"] = {"value": round(f / dt / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.oracle_threads(),
-                               "kind": "oracle", "sample": f"{n} of the 64 tokens over the full vocabulary "
+                               "kind": "oracle", "sample": f"all {n} tokens over the full vocabulary "
                                                            f"({f:.3e} flop, {dt:.1f} s, FP64)"}
     del x
     return res

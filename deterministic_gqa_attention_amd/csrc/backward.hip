@@ -106,8 +106,8 @@ __global__ __launch_bounds__(kDqWaves * 64) void bwd_dq_kernel(const BackwardArg
 
   const int n_bh = a.B * a.Hkv * a.hsubs;
   const int64_t wg = blockIdx.x;
-  const int bh = static_cast<int>(wg % n_bh);
-  const int ptile = a.n_qtiles - 1 - static_cast<int>(wg / n_bh);  // heaviest tiles first
+  int bh, ptile;
+  heavy_first_tile(wg, n_bh, a.n_qtiles, bh, ptile);
   const int b = bh / (a.Hkv * a.hsubs);
   const int hk = (bh / a.hsubs) % a.Hkv;
   const int hs = bh % a.hsubs;

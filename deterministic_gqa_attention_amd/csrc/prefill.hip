@@ -252,9 +252,6 @@ struct TileMap {
   int64_t qpos;
 };
 
-// (b, kv head) pairs an XCD works on at a time (see map_tile)
-constexpr int kXcdPairs = 2;
-
 __device__ __forceinline__ TileMap map_tile(const PrefillArgs& a, int64_t wg) {
   TileMap m;
   // wave index made provably uniform, so per-wave decisions are scalar branches
@@ -262,21 +259,7 @@ __device__ __forceinline__ TileMap map_tile(const PrefillArgs& a, int64_t wg) {
   const int col = threadIdx.x & 31;
   const int n_bh = a.B * a.Hkv * a.hsubs;
   int bh, ptile;
-  if (n_bh % (8 * kXcdPairs) == 0) {
-    // Workgroup wg runs on XCD wg % 8, which owns the (b, kv head) pairs
-    // bh = XCD + 8i.  It takes them kXcdPairs at a time, heaviest tiles
-    // first within each group, so the tiles in flight on one XCD read the
-    // K/V of two pairs (4 MiB at S=4096) rather than of all of its pairs,
-    // and the re-reads of a block by later tiles mostly hit that XCD's L2.
-    const int64_t k = wg >> 3;
-    const int64_t per_group = static_cast<int64_t>(kXcdPairs) * a.n_ptiles;
-    const int r = static_cast<int>(k % per_group);
-    bh = static_cast<int>(wg & 7) + 8 * (static_cast<int>(k / per_group) * kXcdPairs + r % kXcdPairs);
-    ptile = a.n_ptiles - 1 - r / kXcdPairs;
-  } else {
-    bh = static_cast<int>(wg % n_bh);
-    ptile = a.n_ptiles - 1 - static_cast<int>(wg / n_bh);  // heaviest tiles first
-  }
+  heavy_first_tile(wg, n_bh, a.n_ptiles, bh, ptile);
   m.b = bh / (a.Hkv * a.hsubs);
   m.hk = (bh / a.hsubs) % a.Hkv;
   const int hs = bh % a.hsubs;

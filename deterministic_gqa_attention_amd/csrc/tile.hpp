@@ -271,6 +271,29 @@ struct PagedBufLoader {
   }
 };
 
+// Tile order of a grid of n_tiles query tiles x n_bh (b, kv head[, head
+// subgroup]) pairs, heaviest tile (the last) first.  Workgroup wg runs on XCD
+// wg % 8.  When n_bh is a multiple of 16, the XCD owns the pairs bh = XCD + 8i
+// and takes them two at a time, heaviest tiles first within the pair group,
+// so the tiles in flight on one XCD read the K/V of two pairs instead of all
+// of its pairs and a block's re-reads by later tiles mostly hit that XCD's
+// L2; otherwise the grid is tile-major over all pairs.  Either way the map is
+// a bijection of the grid and changes nothing a row computes.
+constexpr int kXcdPairs = 2;
+
+__device__ __forceinline__ void heavy_first_tile(int64_t wg, int n_bh, int n_tiles, int& bh, int& tile) {
+  if (n_bh % (8 * kXcdPairs) == 0) {
+    const int64_t k = wg >> 3;
+    const int64_t per_group = static_cast<int64_t>(kXcdPairs) * n_tiles;
+    const int r = static_cast<int>(k % per_group);
+    bh = static_cast<int>(wg & 7) + 8 * (static_cast<int>(k / per_group) * kXcdPairs + r % kXcdPairs);
+    tile = n_tiles - 1 - r / kXcdPairs;
+  } else {
+    bh = static_cast<int>(wg % n_bh);
+    tile = n_tiles - 1 - static_cast<int>(wg / n_bh);
+  }
+}
+
 // Wait until at most n of this wave's vector-memory loads are outstanding
 // (they retire in issue order); n is one of 0, NI, 2*NI of a loader, chosen
 // by a wave-uniform branch so the count stays an immediate.

@@ -88,6 +88,12 @@ def test_backward_parity_gqa4_causal_ragged():
     _parity_case(11, 2, 200, 8, 2, what="G4 causal ragged")
 
 
+def test_backward_parity_grouped_tile_order():
+    """B*Hkv = 16: the dQ walk takes the grouped tile order; 4 row tiles, the
+    last ragged."""
+    _parity_case(12, 2, 200, 32, 8, what="grouped tile order")
+
+
 def test_backward_parity_tp2_shard_fp32_out_noncausal():
     """The TP=2 local head shard (Hq=16, Hkv=4), non-causal, forward Out in fp32."""
     _parity_case(21, 1, 160, 16, 4, causal=False, out_dtype=torch.float32, what="TP2 non-causal fp32 Out")

@@ -76,6 +76,15 @@ def test_group_sizes(Hq, Hkv, out_dtype):
     _run_and_check(q, k, v, block=128, out_dtype=out_dtype, what=f"group Hq={Hq} Hkv={Hkv}")
 
 
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])
+def test_grouped_tile_order_ragged(out_dtype):
+    """B*Hkv = 16 takes the grouped tile order (each XCD's (b, kv head) pairs
+    two at a time); with 5 position tiles of which the last is ragged, every
+    row still matches the oracle."""
+    q, k, v = _rand(16, (2, 300, 32, 128)), _rand(17, (2, 300, 8, 128)), _rand(18, (2, 300, 8, 128))
+    _run_and_check(q, k, v, block=128, out_dtype=out_dtype, what="grouped tile order, ragged")
+
+
 @pytest.mark.parametrize("block", [64, 128])
 @pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32], ids=["bf16", "fp32"])
 def test_non_causal(block, out_dtype):
